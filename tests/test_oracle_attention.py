@@ -1,0 +1,220 @@
+"""Pins of the oracle's fp64 attention: brute force, a library special case,
+closed forms and invariances."""
+
+import math
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.attention as oatt
+from oracle import layout, zigzag_meta
+
+
+def _textbook_causal(q, k, v, scale):
+    """Full-sequence causal attention written as a per-row loop with math.exp
+    (tiny inputs only).  q [L, Hq, D], k/v [L, Hkv, D]; head h uses KV head
+    h // (Hq/Hkv)."""
+    L, hq, d = q.shape
+    g = hq // k.shape[1]
+    out = np.zeros((L, hq, d))
+    for h in range(hq):
+        for i in range(L):
+            s = [scale * float(np.dot(q[i, h], k[j, h // g])) for j in range(i + 1)]
+            mx = max(s)
+            w = [math.exp(x - mx) for x in s]
+            z = sum(w)
+            for j in range(i + 1):
+                out[i, h] += (w[j] / z) * v[j, h // g]
+    return out
+
+
+def _union_over_ranks(cp, lens, hq, hkv, d, seed, prefix=None):
+    """Every rank's share, gathered rank-major and reranged, against the
+    full-sequence textbook result."""
+    rng = np.random.default_rng(seed)
+    prefix = prefix or [0] * len(lens)
+    full = [p + e for p, e in zip(prefix, lens)]
+    qs = [rng.standard_normal((n, hq, d)) for n in full]
+    ks = [rng.standard_normal((n, hkv, d)) for n in full]
+    vs = [rng.standard_normal((n, hkv, d)) for n in full]
+    scale = 1 / math.sqrt(d)
+    # extend rows of every sequence, concatenated in original order
+    q_ext = np.concatenate([q[p:] for q, p in zip(qs, prefix)], axis=0)
+    m0 = zigzag_meta.build(cp, 0, sum(lens), seq_lens=full, extend_lens=lens)
+    outs = []
+    for m in layout.all_rank_metas(m0):
+        q_loc = layout.shard(q_ext, m)
+        outs.append(oatt.zigzag_rank(q_loc, ks, vs, m, scale))
+    o_gath = np.concatenate(
+        [np.concatenate([o, np.zeros((m0.max_rank_len[0] - o.shape[0],) + o.shape[1:])])
+         for o in outs], axis=0)
+    o_orig = layout.rerange(o_gath, m0)
+    ref = np.concatenate([_textbook_causal(q, k, v, scale)[p:]
+                          for q, k, v, p in zip(qs, ks, vs, prefix)], axis=0)
+    return o_orig, ref
+
+
+@pytest.mark.parametrize("cp", [2, 3, 4, 8])
+def test_union_of_ranks_equals_full_causal_attention(cp):
+    rng = random.Random(cp)
+    for trial in range(3):
+        bs = rng.randint(1, 3)
+        lens = [rng.randint(2 * cp, 2 * cp + 11) for _ in range(bs)]   # uneven blocks included
+        hkv = rng.choice([1, 2])
+        got, ref = _union_over_ranks(cp, lens, 2 * hkv if trial else hkv, hkv, 4, seed=trial)
+        assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_union_with_cached_prefix():
+    got, ref = _union_over_ranks(2, [9, 12], 2, 1, 4, seed=4, prefix=[5, 0])
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_planted_top_left_alignment_is_caught(monkeypatch):
+    """A plausible mistake -- aligning each half's causal mask top-left instead
+    of bottom-right -- must fail the brute-force union check."""
+    orig = oatt.attention_rows
+
+    def top_left(q, rows, k, v, q_len, kv_len, causal, scale, block=256):
+        return orig(q, rows, k, v, kv_len, kv_len, causal, scale, block)  # offset 0
+
+    monkeypatch.setattr(oatt, "attention_rows", top_left)
+    got, ref = _union_over_ranks(2, [16], 2, 1, 4, seed=1)
+    assert np.max(np.abs(got - ref)) > 1e-3
+
+
+def test_matches_torch_sdpa_float64():
+    """Library special case: torch's scaled_dot_product_attention in float64
+    with an explicit bottom-right boolean mask (causal) or none."""
+    rng = np.random.default_rng(3)
+    for q_len, kv_len, hq, hkv, causal in [(7, 19, 4, 2, True), (16, 16, 2, 2, True),
+                                           (5, 33, 8, 1, False), (12, 40, 4, 4, False)]:
+        d = 8
+        q = rng.standard_normal((q_len, hq, d))
+        k = rng.standard_normal((kv_len, hkv, d))
+        v = rng.standard_normal((kv_len, hkv, d))
+        scale = 0.37
+        got = oatt.attention(q, k, v, causal=causal, scale=scale)
+        g = hq // hkv
+        tq = torch.from_numpy(q).permute(1, 0, 2)
+        tk = torch.from_numpy(np.repeat(k, g, axis=1)).permute(1, 0, 2)
+        tv = torch.from_numpy(np.repeat(v, g, axis=1)).permute(1, 0, 2)
+        mask = None
+        if causal:
+            i = torch.arange(q_len)[:, None]
+            j = torch.arange(kv_len)[None, :]
+            mask = j <= i + (kv_len - q_len)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, attn_mask=mask, scale=scale).permute(1, 0, 2).numpy()
+        assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_closed_forms():
+    rng = np.random.default_rng(8)
+    d, hq, hkv = 8, 4, 2
+    k = rng.standard_normal((20, hkv, d))
+    v = rng.standard_normal((20, hkv, d))
+    # the first token of a sequence sees only itself: O = V_0
+    q = rng.standard_normal((20, hq, d))
+    o = oatt.attention(q, k, v, causal=True, scale=0.5)
+    for h in range(hq):
+        assert np.allclose(o[0, h], v[0, h // 2], atol=1e-14)
+    # Q = 0: uniform weights over the visible prefix
+    o = oatt.attention(np.zeros((6, hq, d)), k, v, causal=True, scale=0.5, kv_len=15)
+    for i in range(6):
+        vis = i + 15 - 6 + 1
+        for h in range(hq):
+            assert np.allclose(o[i, h], v[:vis, h // 2].mean(axis=0), atol=1e-13)
+    # all keys equal: uniform weights as well
+    keq = np.repeat(k[:1], 20, axis=0)
+    o = oatt.attention(q[:6], keq, v, causal=False, scale=0.5, kv_len=11)
+    for h in range(hq):
+        assert np.allclose(o[:, h], np.broadcast_to(v[:11, h // 2].mean(axis=0), (6, d)), atol=1e-13)
+
+
+def test_head_mappings():
+    rng = np.random.default_rng(2)
+    d = 8
+    q = rng.standard_normal((9, 8, d))
+    k = rng.standard_normal((14, 2, d))
+    v = rng.standard_normal((14, 2, d))
+    # GQA == MHA with each KV head repeated over a consecutive group of query heads
+    o = oatt.attention(q, k, v, causal=True, scale=0.3)
+    o_mha = oatt.attention(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), causal=True, scale=0.3)
+    assert np.max(np.abs(o - o_mha)) < 1e-14
+    # MHA is the identity mapping: head h alone gives the same as head h in the batch
+    km = np.repeat(k, 4, axis=1)
+    vm = np.repeat(v, 4, axis=1)
+    for h in range(8):
+        oh = oatt.attention(q[:, h:h + 1], km[:, h:h + 1], vm[:, h:h + 1], causal=True, scale=0.3)
+        assert np.max(np.abs(oh[:, 0] - o_mha[:, h])) < 1e-14
+    # MQA: one KV head serves every query head
+    o1 = oatt.attention(q, k[:, :1], v[:, :1], causal=False, scale=0.3)
+    for h in range(8):
+        oh = oatt.attention(q[:, h:h + 1], k[:, :1], v[:, :1], causal=False, scale=0.3)
+        assert np.max(np.abs(oh[:, 0] - o1[:, h])) < 1e-14
+    # a plausible mistake, interleaved groups (h % H_kv), differs
+    k_il = k[:, [h % 2 for h in range(8)]]
+    v_il = v[:, [h % 2 for h in range(8)]]
+    o_il = oatt.attention(q, k_il, v_il, causal=True, scale=0.3)
+    assert np.max(np.abs(o_il - o)) > 1e-3
+
+
+@pytest.mark.parametrize("hkv,ok", [(32, True), (8, True), (1, True), (5, False)])
+def test_head_ratio_contract(hkv, ok):
+    """The GQA report's matrix: 32/32, 32/8, 32/1 accepted; 32/5 rejected."""
+    if ok:
+        assert oatt.check_heads(32, hkv) == 32 // hkv
+    else:
+        with pytest.raises(ValueError):
+            oatt.check_heads(32, hkv)
+
+
+def test_key_shift_invariance():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((10, 2, 8))
+    k = rng.standard_normal((25, 1, 8))
+    v = rng.standard_normal((25, 1, 8))
+    c = rng.standard_normal(8) * 3
+    o1 = oatt.attention(q, k, v, causal=True, scale=0.4)
+    o2 = oatt.attention(q, k + c, v, causal=True, scale=0.4)
+    assert np.max(np.abs(o1 - o2)) < 1e-12
+
+
+def test_row_sampling_equals_full_share():
+    rng = np.random.default_rng(6)
+    lens = [24, 40]
+    m = zigzag_meta.build(2, 1, sum(lens), extend_lens=lens)
+    qloc = rng.standard_normal((m.per_rank_actual_token[1], 4, 8))
+    ks = [rng.standard_normal((n, 2, 8)) for n in lens]
+    vs = [rng.standard_normal((n, 2, 8)) for n in lens]
+    full = oatt.zigzag_rank(qloc, ks, vs, m, 0.3)
+    rows = [0, 5, 13, 20, 31]
+    assert np.max(np.abs(oatt.zigzag_rank_rows(qloc, rows, ks, vs, m, 0.3) - full[rows])) < 1e-14
+
+
+def test_allgather_kv_pad_suffix_and_pad_rows():
+    """AllGather-KV: K/V rows past kv_real (NaN here) are never consumed;
+    local query rows past q_real are zeros; real rows equal plain attention
+    over the real prefix."""
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((12, 4, 8))
+    k = rng.standard_normal((40, 2, 8))
+    v = rng.standard_normal((40, 2, 8))
+    k[33:] = np.nan
+    v[33:] = np.nan
+    o = oatt.allgather_kv(q, k, v, q_real=9, kv_real=33, scale=0.3)
+    assert not np.any(np.isnan(o))
+    assert np.all(o[9:] == 0)
+    ref = oatt.attention(q[:9], k[:33], v[:33], causal=False, scale=0.3)
+    assert np.max(np.abs(o[:9] - ref)) < 1e-14
+    sub = oatt.allgather_kv(q, k, v, q_real=9, kv_real=33, scale=0.3, rows=[1, 10, 4])
+    assert np.array_equal(sub, o[[1, 10, 4]])
+
+
+def test_useful_pairs_closed_forms():
+    assert oatt.useful_pairs(5, 5, True) == 15
+    assert oatt.useful_pairs(4, 10, True) == sum(range(7, 11))
+    assert oatt.useful_pairs(8192, 30000, False) == 8192 * 30000
