@@ -1,0 +1,143 @@
+"""GPU parity of cp_zigzag_rerange and cp_kv_scatter: bit-exact against the oracle."""
+
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import context_prefill_attention_amd as cpa
+import synth
+from oracle import layout, zigzag_meta
+from tests import gpu_cases as gc
+
+pytestmark = pytest.mark.gpu
+
+SENT = np.int16(0x7FC0)   # a bf16 NaN bit pattern, used for pads and untouched memory
+
+
+def _variants():
+    rng = random.Random(17)
+    out = [(2, [256], 2 * 64 * 2), (2, [8192], 4 * 128 * 2), (4, synth.sequence_lengths(synth.WORKLOADS["varlen_cp4_bs8"]), 4 * 128 * 2)]
+    for _ in range(10):
+        cp = rng.choice([2, 3, 4, 5, 8])
+        bs = rng.randint(1, 4)
+        lens = [rng.randint(2 * cp, 2 * cp * 30 + 11) for _ in range(bs)]
+        out.append((cp, lens, rng.choice([16, 48, 256, 2048, 8192])))
+    return out
+
+
+@pytest.mark.parametrize("cp,lens,row_bytes", _variants())
+def test_rerange_both_directions_bit_exact(cp, lens, row_bytes):
+    total = sum(lens)
+    w = row_bytes // 2
+    x = np.random.default_rng(len(lens)).integers(-2**15, 2**15, size=(total, w), dtype=np.int16)
+    mo = zigzag_meta.build(cp, 0, total, extend_lens=lens)
+    meta = cpa.meta_build(cp, 0, lens, device="cuda")
+    g_ref = layout.gathered_buffer(x, mo, pad_value=SENT)
+    # forward: gathered -> original
+    src = torch.from_numpy(g_ref).cuda()
+    dst = torch.full((total, w), int(SENT), dtype=torch.int16, device="cuda")
+    cpa.zigzag_rerange(meta, src, dst, cpa.GATHERED_TO_ORIG)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy(), layout.rerange(g_ref, mo))
+    # inverse: original -> every rank's shard in the gathered layout; pads untouched
+    blank = np.full_like(g_ref, 0x1234)
+    dst2 = torch.from_numpy(blank).cuda()
+    cpa.zigzag_rerange(meta, torch.from_numpy(x).cuda(), dst2, cpa.ORIG_TO_GATHERED)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst2.cpu().numpy(), layout.rerange_inverse(x, mo, blank))
+
+
+def test_rerange_config4_kv_full_size():
+    """K and V of the long-context workload: [131072, 8, 128] bf16 each."""
+    w = synth.WORKLOADS["long_cp8_s131072_r3"]
+    total = w.seq_len
+    mo = zigzag_meta.build(w.cp_size, 3, total)
+    meta = cpa.meta_build(w.cp_size, 3, [total], device="cuda")
+    _, k, v = synth.normal_bf16(w.seed, (1, 1, 1), (total, w.h_kv, w.d), (total, w.h_kv, w.d))
+    for t in (k, v):
+        xb = gc.bits(t)
+        g_ref = layout.gathered_buffer(xb, mo, pad_value=SENT)
+        dst = torch.empty((total, w.h_kv, w.d), dtype=torch.bfloat16, device="cuda")
+        cpa.zigzag_rerange(meta, torch.from_numpy(g_ref).view(torch.bfloat16).cuda(), dst, cpa.GATHERED_TO_ORIG)
+        torch.cuda.synchronize()
+        assert np.array_equal(gc.bits(dst), xb)
+
+
+def _scatter_case(cp, lens, h_kv, d, ps, seq=None, seed=0, spare_pages=5):
+    total = sum(lens)
+    mo = zigzag_meta.build(cp, 0, total, seq_lens=seq, extend_lens=lens)
+    full = [p + e for p, e in zip(mo.prefix_offsets, mo.extend_lens)]
+    rng = np.random.default_rng(seed)
+    npg = [(n + ps - 1) // ps for n in full]
+    indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+    n_pool = int(indptr[-1]) + spare_pages
+    indices = rng.permutation(n_pool)[: int(indptr[-1])].astype(np.int32)
+    k = rng.integers(-2**15, 2**15, size=(total, h_kv, d), dtype=np.int16)
+    v = rng.integers(-2**15, 2**15, size=(total, h_kv, d), dtype=np.int16)
+    kg = layout.gathered_buffer(k, mo, pad_value=SENT)
+    vg = layout.gathered_buffer(v, mo, pad_value=SENT)
+    pool0 = np.full((n_pool, ps, h_kv, d), SENT, dtype=np.int16)
+    meta = cpa.meta_build(cp, 0, lens, seq_lens=seq, device="cuda")
+    kp = torch.from_numpy(pool0).cuda().view(torch.bfloat16)
+    vp = torch.from_numpy(pool0).cuda().view(torch.bfloat16)
+    cpa.kv_scatter(meta, torch.from_numpy(kg).cuda().view(torch.bfloat16),
+                   torch.from_numpy(vg).cuda().view(torch.bfloat16), kp, vp, ps,
+                   torch.from_numpy(indptr).cuda(), torch.from_numpy(indices).cuda())
+    torch.cuda.synchronize()
+    k_ref = layout.kv_scatter(kg, mo, pool0, indptr, indices, ps)
+    v_ref = layout.kv_scatter(vg, mo, pool0, indptr, indices, ps)
+    return kp.view(torch.int16).cpu().numpy(), vp.view(torch.int16).cpu().numpy(), k_ref, v_ref
+
+
+@pytest.mark.parametrize("cp,lens,h_kv,d,ps,seq", [
+    (2, [256], 2, 64, 16, None),
+    (4, [40, 57, 104], 4, 128, 16, None),
+    (3, [31, 20], 1, 128, 1, [40, 20]),          # cached prefix, page size 1
+    (8, [200], 8, 128, 64, [264]),
+    (2, [13, 15, 16, 17], 2, 64, 4, [13, 20, 16, 30]),
+])
+def test_scatter_bit_exact_with_sentinels(cp, lens, h_kv, d, ps, seq):
+    kp, vp, k_ref, v_ref = _scatter_case(cp, lens, h_kv, d, ps, seq=seq, seed=cp)
+    assert np.array_equal(kp, k_ref) and np.array_equal(vp, v_ref)
+
+
+def test_scatter_config2_and_config3_shapes():
+    _kp, _vp, k_ref, v_ref = None, None, None, None
+    kp, vp, k_ref, v_ref = _scatter_case(2, [8192], 4, 128, 16, seed=2, spare_pages=0)
+    assert np.array_equal(kp, k_ref) and np.array_equal(vp, v_ref)
+    lens = synth.sequence_lengths(synth.WORKLOADS["varlen_cp4_bs8"])
+    kp, vp, k_ref, v_ref = _scatter_case(4, lens, 4, 128, 16, seed=3)
+    assert np.array_equal(kp, k_ref) and np.array_equal(vp, v_ref)
+
+
+def test_scatter_then_attention_end_to_end():
+    """Gathered K/V -> pool (scatter kernel) -> attention kernel, vs the oracle."""
+    import math
+    from oracle import attention as oatt
+    cp, lens, h_q, h_kv, d, ps = 4, [300, 128], 16, 2, 128, 16
+    total = sum(lens)
+    qg, kg, vg = synth.normal_bf16(41, (total, h_q, d), (total, h_kv, d), (total, h_kv, d))
+    m0 = zigzag_meta.build(cp, 0, total, extend_lens=lens)
+    k_gath = layout.gathered_buffer(gc.bits(kg), m0, pad_value=SENT)
+    v_gath = layout.gathered_buffer(gc.bits(vg), m0, pad_value=SENT)
+    w = synth.Workload(name="e2e", seed=41, causal=True, h_q=h_q, h_kv=h_kv, d=d, page_size=ps,
+                       contiguous_kv=False, cp_size=cp)
+    indptr, indices, npages = synth.page_table(w, lens)
+    ip, ix = torch.from_numpy(indptr).cuda(), torch.from_numpy(indices).cuda()
+    kp = torch.zeros(npages, ps, h_kv, d, dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    for r in range(cp):
+        meta = cpa.meta_build(cp, r, lens, attn_group=h_q // h_kv, device="cuda")
+        cpa.kv_scatter(meta, torch.from_numpy(k_gath).cuda().view(torch.bfloat16),
+                       torch.from_numpy(v_gath).cuda().view(torch.bfloat16), kp, vp, ps, ip, ix)
+        mo = zigzag_meta.build(cp, r, total, extend_lens=lens)
+        q_loc = torch.from_numpy(layout.shard(gc.bits(qg), mo)).view(torch.bfloat16)
+        out = torch.empty(q_loc.shape, dtype=torch.bfloat16, device="cuda")
+        cpa.prefill_attn(q_loc.cuda(), kp, vp, out, meta, 1 / math.sqrt(d), ps, ip, ix)
+        torch.cuda.synchronize()
+        ref = oatt.zigzag_rank(q_loc, [kg[starts[b]:starts[b + 1]] for b in range(2)],
+                               [vg[starts[b]:starts[b + 1]] for b in range(2)], mo, 1 / math.sqrt(d))
+        gc.assert_close(out, ref, f"e2e rank {r}")
