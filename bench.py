@@ -1,0 +1,236 @@
+"""Benchmark: one CP rank's share of zigzag prefill attention on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+  1. host zigzag metadata (cp_meta_build) and its one host->device copy,
+  2. KV scatter of the all-gathered K and V into the paged pool,
+  3. zigzag rerange of the gathered K and V back to token order,
+  4. the fused causal attention of both zigzag halves.
+Inputs are resident in HBM before the timed region starts.
+
+Default workload: cp_size=8, one sequence of 131072 tokens (blocks of 8192),
+rank 3 (blocks 3 and 12; kv_len 32768 and 106496), H_q=64, H_kv=8, D=128,
+paged KV with page size 64 and permuted pages, bf16.
+
+Prints one JSON line.  ``value`` is useful attention TFLOP/s over the whole
+step (masked-out pairs and skipped tiles are not counted).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+
+def causal_pairs(q_len: int, kv_len: int) -> int:
+    """(query, visible key) pairs of one causal bottom-right segment, closed form."""
+    off = kv_len - q_len
+    # sum_{i=0}^{q_len-1} (i + off + 1)
+    return q_len * (off + 1) + q_len * (q_len - 1) // 2
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_cp8_s131072_r3")
+    ap.add_argument("--rank", type=int, default=None, help="CP rank (zigzag workloads)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=768, help="query rows in the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def calibrate_copy(steps: int) -> None:
+    """A plain copy of known size: 1 GiB read + 1 GiB written per launch.
+    Profiler byte counters of this run scale the attention kernel's counters."""
+    import torch
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": src.numel() * 2, "calibrate_copy_bytes_written":
+                      dst.numel() * 2, "launches": steps}))
+
+
+def traffic_for(kernel_src: str):
+    """Measured HBM bytes per attention launch, if the committed counter
+    summary was taken on this exact kernel source."""
+    path = os.path.join(ROOT, "profiles", "attn_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("kernel_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, meta_lists, q_loc, k_seq, v_seq, n_rows: int):
+    """Time the fp64 oracle on an evenly spaced sample of query rows of the
+    same rank share; scale to useful TFLOP/s."""
+    import numpy as np
+    from oracle import attention as oatt
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    segs = meta_lists["segments"]
+    per = max(1, n_rows // len(segs))
+    scale = 1.0 / math.sqrt(w.d)
+    q_cpu = q_loc.cpu()
+    k64 = k_seq.to(dtype=__import__("torch").float64).numpy()
+    v64 = v_seq.to(dtype=__import__("torch").float64).numpy()
+    flops = 0
+    t0 = time.perf_counter()
+    for (r0, q_len, kv_len) in segs:
+        loc = np.linspace(0, q_len - 1, per).astype(np.int64)
+        oatt.attention_rows(q_cpu[(r0 + loc).tolist()], loc, k64, v64, q_len, kv_len, True, scale)
+        off = kv_len - q_len
+        flops += 4 * w.d * w.h_q * int(np.sum(loc + off + 1))
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{per * len(segs)} query rows ({per} evenly spaced per zigzag half) x {w.h_q} heads "
+                      f"of the same rank share, all visible keys, numpy float64; {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.steps)
+        return
+    import torch
+    import context_prefill_attention_amd as cpa
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if not w.causal:
+        print("bench.py times the zigzag (causal) workloads", file=sys.stderr)
+        sys.exit(2)
+    rank = w.ranks[0] if args.rank is None else args.rank
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    lens = synth.sequence_lengths(w)
+    total = sum(lens)
+    group = w.h_q // w.h_kv
+
+    m0 = cpa.meta_build(w.cp_size, rank, lens, attn_group=group)
+    n_loc, n_g = m0.n_local_rows, w.cp_size * m0.max_rank_len
+    q_loc, k_g, v_g = synth.normal_bf16(w.seed, (n_loc, w.h_q, w.d), (n_g, w.h_kv, w.d), (n_g, w.h_kv, w.d))
+    indptr, indices, n_pages = synth.page_table(w, lens)
+    q_d, k_gd, v_gd = q_loc.to(dev), k_g.to(dev), v_g.to(dev)
+    ip, ix = torch.from_numpy(indptr).to(dev), torch.from_numpy(indices).to(dev)
+    k_pool = torch.zeros(n_pages, w.page_size, w.h_kv, w.d, dtype=torch.bfloat16, device=dev)
+    v_pool = torch.zeros_like(k_pool)
+    k_orig = torch.empty(total, w.h_kv, w.d, dtype=torch.bfloat16, device=dev)
+    v_orig = torch.empty_like(k_orig)
+    out = torch.empty_like(q_d)
+    scale = 1.0 / math.sqrt(w.d)
+
+    segs = [(m0.cu_seqlens_q_prev[b], m0.q_prev[b], m0.kv_len_prev[b]) for b in range(m0.bs)] + \
+           [(m0.total_q_prev_tokens + m0.cu_seqlens_q_next[b], m0.q_next[b], m0.kv_len_next[b])
+            for b in range(m0.bs)]
+    pairs = sum(causal_pairs(q, kv) for (_r, q, kv) in segs)
+    useful_flops = 4 * w.d * w.h_q * pairs
+    row_bytes = w.h_kv * w.d * 2
+    rerange_bytes = 2 * 2 * total * row_bytes      # K and V, each read once and written once
+    scatter_bytes = 2 * 2 * total * row_bytes
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    stats = {"scatter": 0.0, "rerange": 0.0, "attn": 0.0}
+
+    def step(record: bool):
+        meta = cpa.meta_build(w.cp_size, rank, lens, attn_group=group, device=dev)
+        if record:
+            ev[0].record()
+        cpa.kv_scatter(meta, k_gd, v_gd, k_pool, v_pool, w.page_size, ip, ix)
+        if record:
+            ev[1].record()
+        cpa.zigzag_rerange(meta, k_gd, k_orig, cpa.GATHERED_TO_ORIG)
+        cpa.zigzag_rerange(meta, v_gd, v_orig, cpa.GATHERED_TO_ORIG)
+        if record:
+            ev[2].record()
+        cpa.prefill_attn(q_d, k_pool, v_pool, out, meta, scale, w.page_size, ip, ix)
+        if record:
+            ev[3].record()
+        return meta
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()   # per step, so the events of every step can be read
+        stats["scatter"] += ev[0].elapsed_time(ev[1])
+        stats["rerange"] += ev[1].elapsed_time(ev[2])
+        stats["attn"] += ev[2].elapsed_time(ev[3])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    attn_ms = stats["attn"] / args.steps
+    rer_ms = stats["rerange"] / args.steps
+    sc_ms = stats["scatter"] / args.steps
+    if not torch.isfinite(out).all():
+        print("non-finite attention output", file=sys.stderr)
+        sys.exit(1)
+
+    attn_tflops = useful_flops / (attn_ms * 1e-3) / 1e12
+    kernel_src = os.path.join(ROOT, "context_prefill_attention_amd", "csrc", "cp_attn.hip")
+    res = {
+        "metric": "CP-rank prefill attn useful TFLOP/s (% MI355X bf16 MFMA peak); rerange GB/s",
+        "value": round(useful_flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "cp_size": w.cp_size, "cp_rank": rank, "bs": len(lens),
+                   "seq_len": total, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.d,
+                   "page_size": w.page_size, "parallelism": "one CP rank's share on one GPU"},
+        "attn_ms": round(attn_ms, 4),
+        "attn_useful_tflops": round(attn_tflops, 2),
+        "attn_frac_of_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "rerange_kv_ms": round(rer_ms, 4),
+        "rerange_gbps": round(rerange_bytes / (rer_ms * 1e-3) / 1e9, 1),
+        "scatter_kv_ms": round(sc_ms, 4),
+        "scatter_gbps": round(scatter_bytes / (sc_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for(kernel_src)},
+    }
+    if not args.no_cpu_baseline:
+        # the oracle reads synthetic token-order K/V of the same shape (its
+        # timing does not depend on the values)
+        res["cpu_baseline"] = cpu_baseline(w, {"segments": segs}, q_loc, k_g[:total], v_g[:total],
+                                           args.cpu_rows)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
