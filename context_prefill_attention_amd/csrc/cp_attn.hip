@@ -32,7 +32,14 @@
 // LDS: K and V tiles of 64 keys x D, double buffered (64 KiB at D = 128), rows
 // of D*2 bytes with the 16-byte chunk index XOR-swizzled by the row so that
 // both the K reads (16 rows, same chunk) and the transposed V reads (4 rows x
-// 4 chunks) hit distinct banks.
+// 4 chunks) hit distinct banks.  Tiles arrive by direct global->LDS loads
+// (global_load_lds_dwordx4) issued one tile ahead; the page ids they need are
+// fetched two tiles ahead, so no load result is waited on before the end of
+// the tile that hides it.
+//
+// Online softmax: the running max is raised only when a row's max grows by
+// more than 2^8 (in exp2 units), so the O/l rescale is a rare wave-uniform
+// branch instead of 64 multiplies per tile.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -108,15 +115,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   constexpr int DBLK = D / 32;            // 32-row blocks of O^T
   constexpr int ROW_BYTES = D * 2;
   constexpr int TILE_BYTES = kAttnKeys * ROW_BYTES;
-  constexpr int LOADS = kAttnKeys * NC / kThreads;   // 16-byte loads per lane per K (or V) tile
-  static_assert(LOADS >= 1 && kAttnKeys * NC % kThreads == 0, "loader shape");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2][2][TILE_BYTES];  // [buf][K,V]
+  constexpr int LOADS = TILE_BYTES / (kThreads * 16);  // 16-byte direct loads per lane per K (or V) tile
+  static_assert(LOADS >= 1 && TILE_BYTES % (kThreads * 16) == 0, "loader shape");
+  // [buf][K,V] tiles.  A direct global->LDS load writes 1 KiB per wave
+  // instruction, lane i at +16*i; the lane picks the global chunk that the
+  // swizzle puts in that slot.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2][TILE_BYTES];
 
   const int h_kv = a.h_kv, group = a.group;
   const int kvh = blockIdx.x % h_kv;
   const Work w = a.work[blockIdx.x / h_kv];
   const Seg s = a.segs[w.seg];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
 
   // This lane's query row: position pos of the item, query head hg of the group.
@@ -143,41 +154,51 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     }
   }
 
-  // Loader geometry: this lane stages chunk (row_u, chunk) of each tile, u < LOADS.
-  const int ld_chunk = tid % NC;
-  const int ld_row0 = tid / NC;                     // row of u = 0; u adds kThreads/NC rows
-  constexpr int ROW_STEP = kThreads / NC;
-  const int32_t* ptab = a.indices + a.indptr[s.page_row];
-  const int ps_mask = (1 << a.page_shift) - 1;
-  const int64_t head_off = (int64_t)kvh * ROW_BYTES + ld_chunk * 16;
-  const int64_t tok_stride = (int64_t)h_kv * ROW_BYTES;
+  // Zero both buffers once: rows past kv_len are never loaded, and must hold
+  // finite values (the masked scores select -inf, the zero probabilities
+  // multiply V).  Later partial tiles keep finite rows of an earlier tile.
+  {
+    u32x4* z = reinterpret_cast<u32x4*>(&smem[0][0][0]);
+#pragma unroll
+    for (int i = tid; i < 4 * TILE_BYTES / 16; i += kThreads) z[i] = u32x4{0, 0, 0, 0};
+  }
 
-  auto page_of = [&](int key) -> int {
-    if (key >= s.kv_len) return -1;
-    const int pg = ptab[key >> a.page_shift];
-    return (pg >= 0 && pg < a.num_pages) ? pg : -1;
+  // Loader geometry: direct load u of this lane writes LDS byte
+  // (u*8 + wave)*1024 + 16*lane of the tile, i.e. one 16-byte slot of key row
+  // ld_row[u]; it fetches the chunk that the swizzle places in that slot.
+  const int32_t* ptab = a.indices + a.indptr[s.page_row];
+  const int shift = a.page_shift;
+  const int ps_mask = (1 << shift) - 1;
+  const int64_t tok_stride = (int64_t)h_kv * ROW_BYTES;
+  int ld_row[LOADS];
+  int64_t ld_off[LOADS];   // byte offset of the chunk within a token row of the pool
+#pragma unroll
+  for (int u = 0; u < LOADS; ++u) {
+    const int o = (u * kWaves + wave) * 1024 + lane * 16;
+    const int row = o / ROW_BYTES, slot = (o % ROW_BYTES) / 16;
+    ld_row[u] = row;
+    ld_off[u] = (int64_t)kvh * ROW_BYTES + (int64_t)(swz<NC>(row, slot)) * 16;  // swz is an involution
+  }
+  // Page ids: with pages of >= 64 keys a tile lies in one page and its id is
+  // one scalar load; smaller pages give each lane its row's page.
+  const bool page_per_tile = shift >= 6;
+  auto page_id = [&](int t, int u) -> int {
+    const int key = t * kAttnKeys + ld_row[u];
+    if (page_per_tile) return ptab[(t * kAttnKeys) >> shift];
+    return key < s.kv_len ? ptab[key >> shift] : 0;
   };
-  auto load_tile = [&](int t, const int* pg, u32x4* kr, u32x4* vr) {
+  auto issue_tile = [&](int t, int buf, const int* pg) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
-      const int key = t * kAttnKeys + ld_row0 + u * ROW_STEP;
-      if (pg[u] >= 0) {
-        const int64_t off = ((int64_t)pg[u] << a.page_shift | (key & ps_mask)) * tok_stride + head_off;
-        kr[u] = *reinterpret_cast<const u32x4*>(a.k_pool + off);
-        vr[u] = *reinterpret_cast<const u32x4*>(a.v_pool + off);
-      } else {
-        kr[u] = u32x4{0, 0, 0, 0};  // keys past kv_len: zero rows, never NaN
-        vr[u] = u32x4{0, 0, 0, 0};
+      const int key = t * kAttnKeys + ld_row[u];
+      const int page = pg[u];
+      if (key < s.kv_len && page >= 0 && page < a.num_pages) {
+        const int64_t off = ((int64_t)page << shift | (key & ps_mask)) * tok_stride + ld_off[u];
+        __builtin_amdgcn_global_load_lds(a.k_pool + off,
+            (__attribute__((address_space(3))) void*)&smem[buf][0][(u * kWaves + wave) * 1024], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(a.v_pool + off,
+            (__attribute__((address_space(3))) void*)&smem[buf][1][(u * kWaves + wave) * 1024], 16, 0, 0);
       }
-    }
-  };
-  auto store_tile = [&](int buf, const u32x4* kr, const u32x4* vr) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int row = ld_row0 + u * ROW_STEP;
-      const int off = row * ROW_BYTES + swz<NC>(row, ld_chunk) * 16;
-      *reinterpret_cast<u32x4*>(&smem[buf][0][off]) = kr[u];
-      *reinterpret_cast<u32x4*>(&smem[buf][1][off]) = vr[u];
     }
   };
 
@@ -186,32 +207,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const float c = a.scale_log2;
+  // Rescale threshold: the running max is only raised when a row's max grows
+  // by more than 8 in log2 units, so probabilities stay <= 2^8 and O/l are
+  // rescaled rarely (the result is the same softmax with another reference).
+  const float tau = 8.f / c;
   const int n_tiles = w.n_tiles;
 
-  int pg_next[LOADS];   // pages of the tile after the one being computed
+  int pg_next[LOADS];   // page ids of the tile after the one being computed
+  __syncthreads();      // zero fill done before any direct load lands
   if (n_tiles > 0) {
     int pg0[LOADS];
-    u32x4 kr[LOADS], vr[LOADS];
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) pg0[u] = page_of(ld_row0 + u * ROW_STEP);
-    load_tile(0, pg0, kr, vr);
-    store_tile(0, kr, vr);
+    for (int u = 0; u < LOADS; ++u) pg0[u] = page_id(0, u);
+    issue_tile(0, 0, pg0);
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u)
-      pg_next[u] = (n_tiles > 1) ? page_of(kAttnKeys + ld_row0 + u * ROW_STEP) : -1;
+    for (int u = 0; u < LOADS; ++u) pg_next[u] = n_tiles > 1 ? page_id(1, u) : -1;
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
     __syncthreads();
   }
 
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
-    // Issue the next tile's global loads and the page ids of the tile after.
-    u32x4 kr[LOADS], vr[LOADS];
-    const bool has_next = t + 1 < n_tiles;
-    if (has_next) load_tile(t + 1, pg_next, kr, vr);
+    // Issue the next tile's direct loads and fetch the page ids of the tile
+    // after; nothing waits on either until the end of this iteration.
+    if (t + 1 < n_tiles) issue_tile(t + 1, buf ^ 1, pg_next);
     int pg_after[LOADS];
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u)
-      pg_after[u] = (t + 2 < n_tiles) ? page_of((t + 2) * kAttnKeys + ld_row0 + u * ROW_STEP) : -1;
+    for (int u = 0; u < LOADS; ++u) pg_after[u] = (t + 2 < n_tiles) ? page_id(t + 2, u) : -1;
 
     // S^T for the 64 keys of this tile: two 32-key blocks.
     const unsigned char* kt = smem[buf][0];
@@ -241,16 +263,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
         }
     }
 
-    // Online softmax in base 2: p = exp2(s*c - m*c), with m the running max of raw scores.
+    // Online softmax in base 2: p = exp2(s*c - m*c), m a reference no smaller
+    // than 8/c below the row max seen so far.
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][j]);
     mx = wave_half_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-    const float mc = m_new * c;
+    const bool grow = mx > m_run + tau;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = m_run * c;
     float rs = 0.f;
     uint32_t pk[2][8];
 #pragma unroll
@@ -262,10 +292,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
         rs += p0 + p1;
         pk[kb][j >> 1] = pack_bf16x2(p0, p1);
       }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
+    l_run += rs;
 
     // O^T += V^T P^T over the 64 keys, four 16-key steps.  Step st uses C
     // elements 8*(st&1) .. +7 of key block st>>1, i.e. keys
@@ -297,10 +324,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       }
     }
 
-    if (has_next) store_tile(buf ^ 1, kr, vr);
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) pg_next[u] = pg_after[u];
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);   // next tile's direct loads from this wave have landed
+    __syncthreads();                 // ... and from every wave; this tile's reads are done
   }
 
   // Epilogue: O = O^T / l.  Lane (col, half) holds d = 32*db + 8*(j/4) + 4*half + j%4.
