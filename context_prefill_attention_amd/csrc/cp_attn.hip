@@ -43,6 +43,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "../../include/cpattn.h"
 #include "cp_internal.h"
@@ -108,19 +109,48 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-template <int D>
+constexpr int kStages = 4;   // LDS ring depth (tiles); loads run two tiles ahead
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (lgkm and exp counters left unconstrained).
+// Encoding: vmcnt bits 3:0 and 15:14, expcnt bits 6:4, lgkmcnt bits 11:8.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// PAGE_PER_TILE: pages hold >= 64 keys, so a tile lies in one page and its id
+// is one scalar load; otherwise every lane looks up its own row's page.
+template <int D, bool PAGE_PER_TILE>
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   constexpr int NC = D / 8;               // 16-byte chunks per K/V row
   constexpr int KSTEPS = D / 16;          // k-steps of S^T = K Q^T
   constexpr int DBLK = D / 32;            // 32-row blocks of O^T
   constexpr int ROW_BYTES = D * 2;
-  constexpr int TILE_BYTES = kAttnKeys * ROW_BYTES;
+  constexpr int TILE_BYTES = kAttnKeys * ROW_BYTES;    // one K (or V) tile
   constexpr int LOADS = TILE_BYTES / (kThreads * 16);  // 16-byte direct loads per lane per K (or V) tile
+  constexpr int PLOADS = PAGE_PER_TILE ? 0 : LOADS;    // vector page-id loads per lane per tile
   static_assert(LOADS >= 1 && TILE_BYTES % (kThreads * 16) == 0, "loader shape");
-  // [buf][K,V] tiles.  A direct global->LDS load writes 1 KiB per wave
-  // instruction, lane i at +16*i; the lane picks the global chunk that the
-  // swizzle puts in that slot.
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2][TILE_BYTES];
+  // K and V rings of kStages tiles, one array per stage: the compiler can
+  // then tell the stage being read from the stages whose direct loads are
+  // still in flight and does not wait for those loads before the read.  A
+  // direct global->LDS load writes 1 KiB per wave instruction, lane i at
+  // +16*i; the lane picks the global chunk that the swizzle puts in that slot.
+  __shared__ __attribute__((aligned(1024))) unsigned char k_s0[TILE_BYTES], k_s1[TILE_BYTES],
+      k_s2[TILE_BYTES], k_s3[TILE_BYTES], v_s0[TILE_BYTES], v_s1[TILE_BYTES], v_s2[TILE_BYTES],
+      v_s3[TILE_BYTES];
+  static_assert(kStages == 4, "one array per ring stage");
+  auto kbuf = [&](auto stc) -> unsigned char* {
+    constexpr int st = decltype(stc)::value;
+    if constexpr (st == 0) return k_s0; else if constexpr (st == 1) return k_s1;
+    else if constexpr (st == 2) return k_s2; else return k_s3;
+  };
+  auto vbuf = [&](auto stc) -> unsigned char* {
+    constexpr int st = decltype(stc)::value;
+    if constexpr (st == 0) return v_s0; else if constexpr (st == 1) return v_s1;
+    else if constexpr (st == 2) return v_s2; else return v_s3;
+  };
 
   const int h_kv = a.h_kv, group = a.group;
   const int kvh = blockIdx.x % h_kv;
@@ -142,6 +172,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   const int limit = (s.causal && live) ? qp + s.causal_off : s.kv_len - 1;
   // Smallest limit of the item's rows: tiles ending at or below it need no mask.
   const int item_limit = s.causal ? w.p0 + s.causal_off : s.kv_len - 1;
+  const int n_tiles = w.n_tiles;
+  // first tile that holds a key past some row's limit
+  const int t_mask = min(n_tiles, max(0, (item_limit + 1) / kAttnKeys));
 
   bf16x8 qop[KSTEPS];
 #pragma unroll
@@ -154,53 +187,93 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     }
   }
 
-  // Zero both buffers once: rows past kv_len are never loaded, and must hold
-  // finite values (the masked scores select -inf, the zero probabilities
-  // multiply V).  Later partial tiles keep finite rows of an earlier tile.
-  {
-    u32x4* z = reinterpret_cast<u32x4*>(&smem[0][0][0]);
-#pragma unroll
-    for (int i = tid; i < 4 * TILE_BYTES / 16; i += kThreads) z[i] = u32x4{0, 0, 0, 0};
-  }
-
   // Loader geometry: direct load u of this lane writes LDS byte
   // (u*8 + wave)*1024 + 16*lane of the tile, i.e. one 16-byte slot of key row
   // ld_row[u]; it fetches the chunk that the swizzle places in that slot.
-  const int32_t* ptab = a.indices + a.indptr[s.page_row];
+  // The page table is read-only for the whole kernel: read it through the
+  // constant address space so that wave-uniform lookups become scalar loads.
+  typedef const __attribute__((address_space(4))) int32_t cint32;
+  cint32* ptab = (cint32*)(a.indices) + a.indptr[s.page_row];
   const int shift = a.page_shift;
   const int ps_mask = (1 << shift) - 1;
-  const int64_t tok_stride = (int64_t)h_kv * ROW_BYTES;
+  const uint32_t tok_stride = (uint32_t)h_kv * ROW_BYTES;
   int ld_row[LOADS];
-  int64_t ld_off[LOADS];   // byte offset of the chunk within a token row of the pool
+  uint32_t ld_lane[LOADS];   // chunk offset from the head-0 start of the lane's token row
 #pragma unroll
   for (int u = 0; u < LOADS; ++u) {
     const int o = (u * kWaves + wave) * 1024 + lane * 16;
     const int row = o / ROW_BYTES, slot = (o % ROW_BYTES) / 16;
     ld_row[u] = row;
-    ld_off[u] = (int64_t)kvh * ROW_BYTES + (int64_t)(swz<NC>(row, slot)) * 16;  // swz is an involution
+    ld_lane[u] = (uint32_t)(kvh * ROW_BYTES + swz<NC>(row, slot) * 16);  // swz is an involution
   }
-  // Page ids: with pages of >= 64 keys a tile lies in one page and its id is
-  // one scalar load; smaller pages give each lane its row's page.
-  const bool page_per_tile = shift >= 6;
-  auto page_id = [&](int t, int u) -> int {
-    const int key = t * kAttnKeys + ld_row[u];
-    if (page_per_tile) return ptab[(t * kAttnKeys) >> shift];
-    return key < s.kv_len ? ptab[key >> shift] : 0;
+  // Every tile issues exactly LOADS direct loads of K and LOADS of V per
+  // lane (and, with small pages, LOADS page-id loads), whatever the row: rows
+  // past kv_len or with a page id outside the pool are redirected to key 0 of
+  // the sequence (always real and finite) and masked out of the scores.  The
+  // per-wave vector-memory counts are then exact and the waits below can
+  // leave the younger tiles in flight.
+  struct Pages { int p[PAGE_PER_TILE ? 1 : LOADS]; };
+  auto fetch_pages = [&](int t) -> Pages {
+    Pages pg;
+    if constexpr (PAGE_PER_TILE) {
+      pg.p[0] = ptab[(min(t, n_tiles - 1) * kAttnKeys) >> shift];
+    } else {
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) {
+        const int key = min(t * kAttnKeys + ld_row[u], s.kv_len - 1);
+        pg.p[u] = ptab[key >> shift];
+      }
+    }
+    return pg;
   };
-  auto issue_tile = [&](int t, int buf, const int* pg) {
+  const int page0 = ptab[0];
+  const bool page0_ok = page0 >= 0 && page0 < a.num_pages;
+  auto issue_tile = [&](int t, auto stc, const Pages& pg) {
+    unsigned char* kd = kbuf(stc);
+    unsigned char* vd = vbuf(stc);
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int key = t * kAttnKeys + ld_row[u];
-      const int page = pg[u];
-      if (key < s.kv_len && page >= 0 && page < a.num_pages) {
-        const int64_t off = ((int64_t)page << shift | (key & ps_mask)) * tok_stride + ld_off[u];
-        __builtin_amdgcn_global_load_lds(a.k_pool + off,
-            (__attribute__((address_space(3))) void*)&smem[buf][0][(u * kWaves + wave) * 1024], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(a.v_pool + off,
-            (__attribute__((address_space(3))) void*)&smem[buf][1][(u * kWaves + wave) * 1024], 16, 0, 0);
-      }
+      const int page = PAGE_PER_TILE ? pg.p[0] : pg.p[u];
+      const bool ok = key < s.kv_len && page >= 0 && page < a.num_pages;
+      const int64_t tok = ok ? ((int64_t)page << shift | (key & ps_mask))
+                             : (page0_ok ? (int64_t)page0 << shift : 0);
+      const int64_t off = tok * tok_stride + ld_lane[u];
+      __builtin_amdgcn_global_load_lds(a.k_pool + off,
+          (__attribute__((address_space(3))) void*)&kd[(u * kWaves + wave) * 1024], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.v_pool + off,
+          (__attribute__((address_space(3))) void*)&vd[(u * kWaves + wave) * 1024], 16, 0, 0);
     }
   };
+  // Wait until tile t's direct loads have landed, given what this wave
+  // issued after them: the page ids of tile t+2 (with small pages) and the
+  // loads of tile t+1, if those tiles exist.
+  auto wait_tile = [&](int t) {
+    if (t + 2 < n_tiles) wait_vmcnt<PLOADS + 2 * LOADS>();
+    else if (t + 1 < n_tiles) wait_vmcnt<2 * LOADS>();
+    else wait_vmcnt<0>();
+  };
+
+  // LDS read offsets of this lane, fixed for the whole loop (stage, block
+  // and step offsets are immediates):
+  //   K: key row kb*32 + col, chunk 2*ks + half       (kb adds 32 rows)
+  //   V: key row 16*st + 8*e + 4*half + j/4, chunk 4*db + 2*gsub + (j%4)/2,
+  //      8-byte half j%2                              (st adds 16 rows)
+  // 16 rows do not change the swizzle, so both row offsets are additive.
+  uint32_t kofs[KSTEPS], vofs[DBLK][2];
+  {
+    const int j = lane & 15, gsub = (lane >> 4) & 1;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) kofs[ks] = col * ROW_BYTES + swz<NC>(col, ks * 2 + half) * 16;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int row = 8 * e + half * 4 + (j >> 2);
+        const int chunk = db * 4 + gsub * 2 + ((j & 3) >> 1);
+        vofs[db][e] = row * ROW_BYTES + swz<NC>(row, chunk) * 16 + (j & 1) * 8;
+      }
+  }
 
   f32x16 o[DBLK];
 #pragma unroll
@@ -211,128 +284,175 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   // by more than 8 in log2 units, so probabilities stay <= 2^8 and O/l are
   // rescaled rarely (the result is the same softmax with another reference).
   const float tau = 8.f / c;
-  const int n_tiles = w.n_tiles;
+  const uint32_t ones_bf16x2 = 0x3f803f80u;   // (1.0, 1.0) in bf16
 
-  int pg_next[LOADS];   // page ids of the tile after the one being computed
-  __syncthreads();      // zero fill done before any direct load lands
-  if (n_tiles > 0) {
-    int pg0[LOADS];
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) pg0[u] = page_id(0, u);
-    issue_tile(0, 0, pg0);
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) pg_next[u] = n_tiles > 1 ? page_id(1, u) : -1;
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
-    __syncthreads();
-  }
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    // Issue the next tile's direct loads and fetch the page ids of the tile
-    // after; nothing waits on either until the end of this iteration.
-    if (t + 1 < n_tiles) issue_tile(t + 1, buf ^ 1, pg_next);
-    int pg_after[LOADS];
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) pg_after[u] = (t + 2 < n_tiles) ? page_id(t + 2, u) : -1;
-
-    // S^T for the 64 keys of this tile: two 32-key blocks.
-    const unsigned char* kt = smem[buf][0];
-    const unsigned char* vt = smem[buf][1];
-    f32x16 sc[2];
+  // S^T of tile t (stage st): two 32-key blocks of 16 MFMAs each.
+  auto qk = [&](auto stc, f32x16* sc) {
+    const unsigned char* kt = kbuf(stc);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sc[kb] = f32x16{};
-      const int row = kb * 32 + col;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(kt + row * ROW_BYTES + swz<NC>(row, ks * 2 + half) * 16);
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(kt + kofs[ks] + kb * 32 * ROW_BYTES);
         sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qop[ks], sc[kb], 0, 0, 0);
       }
     }
-
-    // Mask keys past each row's limit (only tiles that reach past the item's
-    // smallest limit can hold such keys).
-    const int kbase = t * kAttnKeys;
-    if (kbase + kAttnKeys - 1 > item_limit) {
+  };
+  // O^T += V^T P^T for the tile in stage st: four 16-key steps; step kst uses
+  // C elements 8*(kst&1) .. +7 of key block kst>>1, i.e. keys
+  // 16*kst + 8*(i/4) + 4*half + i%4 for operand slot i.
+  auto pv = [&](auto stc, const uint32_t* pk) {
+    unsigned char* vt = vbuf(stc);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kst = 0; kst < 4; ++kst) {
+      const uint32_t* pp = pk + kst * 4;
+      const bf16x8 pop = __builtin_bit_cast(bf16x8, u32x4{pp[0], pp[1], pp[2], pp[3]});
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = kbase + kb * 32 + (j >> 2) * 8 + half * 4 + (j & 3);
-          if (key > limit) sc[kb][j] = -INFINITY;
-        }
+      for (int db = 0; db < DBLK; ++db) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)((__attribute__((address_space(3))) unsigned char*)vt + vofs[db][0] + kst * 16 * ROW_BYTES));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)((__attribute__((address_space(3))) unsigned char*)vt + vofs[db][1] + kst * 16 * ROW_BYTES));
+        const i16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pop, o[db], 0, 0, 0);
+      }
     }
-
-    // Online softmax in base 2: p = exp2(s*c - m*c), m a reference no smaller
-    // than 8/c below the row max seen so far.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][j]);
-    mx = wave_half_max(mx);
-    const bool grow = mx > m_run + tau;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
-      m_run = m_new;
-    }
-    const float mc = m_run * c;
+  };
+  // Probabilities of one tile against reference m (exp2 domain): packed bf16
+  // in pk (C-element order), their sum (of the rounded values) returned.
+  auto probs = [&](const f32x16* sc, float m, uint32_t* pk) -> float {
+    const float mc = m * c;
     float rs = 0.f;
-    uint32_t pk[2][8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; j += 2) {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][j], c, -mc));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][j + 1], c, -mc));
-        rs += p0 + p1;
-        pk[kb][j >> 1] = pack_bf16x2(p0, p1);
+        const uint32_t pb = pack_bf16x2(p0, p1);
+        pk[kb * 8 + (j >> 1)] = pb;
+        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb),
+                                             __builtin_bit_cast(bf16x2, ones_bf16x2), rs, false);
       }
-    l_run += rs;
-
-    // O^T += V^T P^T over the 64 keys, four 16-key steps.  Step st uses C
-    // elements 8*(st&1) .. +7 of key block st>>1, i.e. keys
-    // 16*st + 8*(i/4) + 4*half + i%4 for operand slot i.
+    return rs;
+  };
+  // Keys past each row's limit leave the scores (tiles from t_mask on).
+  auto mask = [&](int t, f32x16* sc) {
+    const int rel = limit - t * kAttnKeys - half * 4;   // visible key offsets within the tile
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const uint32_t* pp = &pk[st >> 1][(st & 1) * 4];
-      const bf16x8 pop = __builtin_bit_cast(bf16x8, u32x4{pp[0], pp[1], pp[2], pp[3]});
-      // transposed V reads: 16-lane group gsub covers d0 .. d0+15 of a 32-d block
-      const int j = lane & 15;
-      const int gsub = (lane >> 4) & 1;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        i16x4 lo, hi;
-        {
-          const int row = st * 16 + half * 4 + (j >> 2);
-          const int chunk = db * 4 + gsub * 2 + ((j & 3) >> 1);
-          const int off = row * ROW_BYTES + swz<NC>(row, chunk) * 16 + (j & 1) * 8;
-          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((__attribute__((address_space(3))) unsigned char*)vt + off));
-        }
-        {
-          const int row = st * 16 + 8 + half * 4 + (j >> 2);
-          const int chunk = db * 4 + gsub * 2 + ((j & 3) >> 1);
-          const int off = row * ROW_BYTES + swz<NC>(row, chunk) * 16 + (j & 1) * 8;
-          hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((__attribute__((address_space(3))) unsigned char*)vt + off));
-        }
-        const i16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pop, o[db], 0, 0, 0);
-      }
+      for (int j = 0; j < 16; ++j)
+        if (kb * 32 + (j >> 2) * 8 + (j & 3) > rel) sc[kb][j] = -INFINITY;
+  };
+  // Softmax of one tile's (masked) scores: running max, probabilities into
+  // pk with the current reference, and the rare raise of the reference.
+  auto softmax = [&](f32x16* sc, uint32_t* pk) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][j]);
+    mx = wave_half_max(mx);
+    float rs = probs(sc, m_run, pk);
+    const bool grow = mx > m_run + tau;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // rare: raise the reference
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      rs = probs(sc, m_new, pk);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
+      m_run = m_new;
     }
+    l_run += rs;
+  };
 
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) pg_next[u] = pg_after[u];
-    __builtin_amdgcn_s_waitcnt(0);   // next tile's direct loads from this wave have landed
-    __syncthreads();                 // ... and from every wave; this tile's reads are done
+  // Barrier between pipeline steps: this wave's LDS reads are complete, the
+  // direct loads of the tile the next step computes have landed (the caller's
+  // vmcnt wait), and no wave passes until all have.  A plain s_barrier: the
+  // usual __syncthreads would also wait for the younger tiles still in flight.
+  auto step_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // Pipeline.  Tile t lives in ring stage t % 4.  Step t issues the page ids
+  // of tile t+3 and the loads of tile t+2, computes S(t) = QK(t), then the PV
+  // product of tile t-1 (whose probabilities are ready) together with the
+  // softmax of tile t, so each wave's VALU work overlaps its own MFMAs.  The
+  // barrier at the end of step t publishes tile t+1 and retires every read of
+  // tile t-1's stage, which step t+1 refills with tile t+3.  The PV product
+  // of tile t-1 reads the probability registers before the softmax of tile t
+  // overwrites them.
+  uint32_t pk[16];
+  if (n_tiles > 0) {
+    Pages pg0 = fetch_pages(0), pg1 = fetch_pages(1);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    issue_tile(0, I0{}, pg0);
+    Pages pg_next = fetch_pages(2);
+    if (n_tiles > 1) issue_tile(1, I1{}, pg1);
+    wait_tile(0);
+    step_barrier();
+
+    // One pipeline step; MASKED tiles hold keys past some row's limit.
+    auto step = [&](auto stc, auto maskc, int t) {
+      constexpr int st = decltype(stc)::value;   // t % kStages
+      constexpr bool MASKED = decltype(maskc)::value;
+      const Pages pg_after = fetch_pages(t + 3);
+      if (t + 2 < n_tiles) issue_tile(t + 2, std::integral_constant<int, (st + 2) % kStages>{}, pg_next);
+      pg_next = pg_after;
+      f32x16 sc[2];
+      qk(stc, sc);
+      if constexpr (MASKED) mask(t, sc);
+      pv(std::integral_constant<int, (st + kStages - 1) % kStages>{}, pk);
+      softmax(sc, pk);
+      wait_tile(t + 1);
+      step_barrier();
+    };
+    auto step_any = [&](auto maskc, int t) {
+      switch (t & 3) {
+        case 0: step(I0{}, maskc, t); break;
+        case 1: step(I1{}, maskc, t); break;
+        case 2: step(I2{}, maskc, t); break;
+        default: step(I3{}, maskc, t); break;
+      }
+    };
+
+    // Step 0: no previous PV product to overlap.
+    {
+      const Pages pg_after = fetch_pages(3);
+      if (2 < n_tiles) issue_tile(2, I2{}, pg_next);
+      pg_next = pg_after;
+      f32x16 sc[2];
+      qk(I0{}, sc);
+      if (t_mask == 0) mask(0, sc);
+      softmax(sc, pk);
+      wait_tile(1);
+      step_barrier();
+    }
+    int t = 1;
+    const int t_full_end = max(1, t_mask);          // tiles [1, t_mask) need no mask
+    for (; t < t_full_end; ++t) step_any(std::false_type{}, t);
+    for (; t < n_tiles; ++t) step_any(std::true_type{}, t);
+    // The last tile's PV product.
+    switch ((n_tiles - 1) & 3) {
+      case 0: pv(I0{}, pk); break;
+      case 1: pv(I1{}, pk); break;
+      case 2: pv(I2{}, pk); break;
+      default: pv(I3{}, pk); break;
+    }
   }
 
   // Epilogue: O = O^T / l.  Lane (col, half) holds d = 32*db + 8*(j/4) + 4*half + j%4.
   if (!valid) return;
-  const float l_tot = wave_half_sum(l_run);
+  const float l_tot = wave_half_sum(l_run);   // the two lane halves summed different keys
   const float inv = live ? 1.f / l_tot : 0.f;
   unsigned char* orow = a.out + qrow * D * 2;
 #pragma unroll
@@ -401,10 +521,15 @@ extern "C" int cp_prefill_attn(const void* q, const void* k_pool, const void* v_
   while ((1 << shift) < page_size) ++shift;
   args.page_shift = shift;
   args.scale_log2 = scale * 1.4426950408889634f;
-  if (D == 128)
-    hipLaunchKernelGGL(attn_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
+  const bool page_per_tile = shift >= 6;   // pages of >= 64 keys: one page per key tile
+  if (D == 128 && page_per_tile)
+    hipLaunchKernelGGL((attn_kernel<128, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
+  else if (D == 128)
+    hipLaunchKernelGGL((attn_kernel<128, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
+  else if (page_per_tile)
+    hipLaunchKernelGGL((attn_kernel<64, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
   else
-    hipLaunchKernelGGL(attn_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((attn_kernel<64, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(CP_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   return CP_OK;
