@@ -46,7 +46,7 @@ static_assert(sizeof(Work) == 16, "Work layout");
 // Attention tiling shared by the work-list builder and the kernel.
 constexpr int kAttnRows = 256;     // (position, head) rows per workgroup: 8 waves x 32
 constexpr int kAttnKeys = 64;      // keys per KV tile
-constexpr int kMaxGroup = 256;     // H_q / H_kv upper bound
+constexpr int kMaxGroup = kAttnRows;  // H_q / H_kv upper bound (one position per workgroup)
 
 constexpr uint32_t kBlobMagic = 0x31415043u;  // "CPA1"
 constexpr int64_t kBlobAlign = 256;

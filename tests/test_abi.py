@@ -47,6 +47,9 @@ def _cases():
     return cases
 
 
+# (position, query head) rows one attention work item covers
+ROWS_PER_ITEM = 256
+
 LISTS = ["split_list", "zigzag_index", "cp_reverse_index", "reverse_split_len",
          "per_rank_actual_token", "kv_len_prev", "kv_len_next", "q_prev", "q_next",
          "cu_seqlens_q_prev", "cu_seqlens_q_next"]
@@ -105,7 +108,7 @@ def test_segments_and_work_list(group):
         for (q_row0, q_len, q_rows, kv_len, off, page_row, causal, _), (_h, b, r0, ql, kl) in zip(segs, osegs):
             assert (q_row0, q_len, q_rows, kv_len, off, page_row, causal) == (r0, ql, ql, kl, kl - ql, b, 1)
         work = _unpack(m.blob, m.off_work, m.n_work, 4)
-        tq = 256 // group
+        tq = ROWS_PER_ITEM // group
         assert m.q_tile == tq
         seen = {s: np.zeros(segs[s][2], dtype=int) for s in range(len(segs))}
         for s, p0, npos, n_tiles in work:
@@ -131,7 +134,7 @@ def test_allgather_meta():
     seg = _unpack(m.blob, m.off_segs, 1, 8)[0]
     assert tuple(seg[:7]) == (0, 8192, 8192, 30000, 0, 0, 0)
     work = _unpack(m.blob, m.off_work, m.n_work, 4)
-    assert m.n_work == 8192 // 64 and np.all(work[:, 3] == -(-30000 // 64))
+    assert m.n_work == 8192 // (ROWS_PER_ITEM // 4) and np.all(work[:, 3] == -(-30000 // 64))
     m = cpa.allgather_meta_build(100, 70, 33, 32)    # pad query rows 70..99
     work = _unpack(m.blob, m.off_work, m.n_work, 4)
     assert work[:, 2].sum() == 100
