@@ -23,23 +23,29 @@
 // v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 d from LDS, B = Q^T held in
 // registers for the whole key loop), so lane l owns query column l%32 and
 // 16 of the 32 keys of a block; the two lane halves of a column split the
-// keys.  Row max needs one exchange between the halves (v_permlane32_swap);
-// row sums stay per half until the end.  The probabilities are already in
-// the B-operand layout of O^T = V^T P^T, so P never leaves registers; V^T
-// comes from LDS through ds_read_b64_tr_b16.  O^T keeps each query in one
-// lane, so the online-softmax rescale is lane-local as well.
+// keys.  The probabilities are already in the B-operand layout of
+// O^T = V^T P^T, so P never leaves registers; V^T comes from LDS through
+// ds_read_b64_tr_b16.  O^T keeps each query in one lane, so the softmax and
+// its rescale are lane-local apart from one exchange between the lane halves
+// (v_permlane32_swap) per 32-key block.
 //
-// LDS: K and V tiles of 64 keys x D, double buffered (64 KiB at D = 128), rows
-// of D*2 bytes with the 16-byte chunk index XOR-swizzled by the row so that
-// both the K reads (16 rows, same chunk) and the transposed V reads (4 rows x
-// 4 chunks) hit distinct banks.  Tiles arrive by direct global->LDS loads
-// (global_load_lds_dwordx4) issued one tile ahead; the page ids they need are
-// fetched two tiles ahead, so no load result is waited on before the end of
-// the tile that hides it.
+// LDS: a ring of four K and V tile stages, 64 keys x D each (128 KiB at
+// D = 128), rows of D*2 bytes with the 16-byte chunk index XOR-swizzled by
+// the row so that both the K reads (16 rows, same chunk) and the transposed V
+// reads (4 rows x 4 chunks) hit distinct banks.  Tiles arrive by direct
+// global->LDS loads (global_load_lds_dwordx4) issued two tiles ahead; the
+// page ids they need are fetched three tiles ahead, so no load result is
+// waited on before the barrier that publishes its tile.
 //
-// Online softmax: the running max is raised only when a row's max grows by
-// more than 2^8 (in exp2 units), so the O/l rescale is a rare wave-uniform
-// branch instead of 64 multiplies per tile.
+// Software pipeline: each step handles the QK product of tile t and the PV
+// product of tile t-1, in two halves of 16 MFMAs; each half also carries the
+// softmax of one 32-key block, whose VALU work is independent of that half's
+// MFMAs, so the two overlap within the wave.
+//
+// Online softmax: the running max is raised only when a probability against
+// the current one would exceed 2^8, so the O/l rescale is a rare wave-uniform
+// branch instead of 64 multiplies per block.  Row sums are accumulated in
+// fp32 from the unrounded probabilities.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -175,6 +181,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   const int n_tiles = w.n_tiles;
   // first tile that holds a key past some row's limit
   const int t_mask = min(n_tiles, max(0, (item_limit + 1) / kAttnKeys));
+  // Tiles the pipeline runs: n_tiles rounded up to 1 + a multiple of the
+  // ring depth (see the main loop); tiles past n_tiles hold no visible key.
+  const int n_pad = n_tiles > 0 ? 1 + ((n_tiles + 2) & ~3) : 0;
 
   bf16x8 qop[KSTEPS];
 #pragma unroll
@@ -249,8 +258,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   // issued after them: the page ids of tile t+2 (with small pages) and the
   // loads of tile t+1, if those tiles exist.
   auto wait_tile = [&](int t) {
-    if (t + 2 < n_tiles) wait_vmcnt<PLOADS + 2 * LOADS>();
-    else if (t + 1 < n_tiles) wait_vmcnt<2 * LOADS>();
+    if (t + 2 < n_pad) wait_vmcnt<PLOADS + 2 * LOADS>();
+    else if (t + 1 < n_pad) wait_vmcnt<2 * LOADS>();
     else wait_vmcnt<0>();
   };
 
@@ -281,32 +290,40 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c = a.scale_log2;
   // Rescale threshold: the running max is only raised when a row's max grows
-  // by more than 8 in log2 units, so probabilities stay <= 2^8 and O/l are
-  // rescaled rarely (the result is the same softmax with another reference).
-  const float tau = 8.f / c;
-  const uint32_t ones_bf16x2 = 0x3f803f80u;   // (1.0, 1.0) in bf16
+  // by more than 8 in log2 units, i.e. when some probability against the
+  // current reference exceeds 2^8; so O and l are rescaled rarely (the result
+  // is the same softmax with another reference).
+  constexpr float kGrowLimit = 256.f;
 
-  // S^T of tile t (stage st): two 32-key blocks of 16 MFMAs each.
-  auto qk = [&](auto stc, f32x16* sc) {
-    const unsigned char* kt = kbuf(stc);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  // S^T of key block kb (keys 32*kb .. 32*kb+31) of the tile in stage st:
+  // KSTEPS MFMAs over d, K from LDS, Q^T from registers.
+  auto qk_blk = [&](auto stc, auto kbc) -> f32x16 {
+    constexpr int kb = decltype(kbc)::value;
+    const unsigned char* kt = kbuf(stc) + kb * 32 * ROW_BYTES;
+    f32x16 acc = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sc[kb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(kt + kofs[ks] + kb * 32 * ROW_BYTES);
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qop[ks], sc[kb], 0, 0, 0);
-      }
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(kt + kofs[ks]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qop[ks], acc, 0, 0, 0);
     }
+    return acc;
   };
-  // O^T += V^T P^T for the tile in stage st: four 16-key steps; step kst uses
-  // C elements 8*(kst&1) .. +7 of key block kst>>1, i.e. keys
-  // 16*kst + 8*(i/4) + 4*half + i%4 for operand slot i.
-  auto pv = [&](auto stc, const uint32_t* pk) {
+  // O^T += V^T P^T over key block kb of the tile in stage st, P of that
+  // block in pb (8 registers of packed bf16 pairs, C-element order).  Two
+  // 16-key steps; step kk uses C elements 8*kk .. 8*kk+7 of the block, i.e.
+  // keys 32*kb + 16*kk + 8*(i/4) + 4*half + i%4 for operand slot i.
+  auto pv_blk = [&](auto stc, auto kbc, const uint32_t* pb) {
+    constexpr int kb = decltype(kbc)::value;
     unsigned char* vt = vbuf(stc);
 #pragma unroll
-    for (int kst = 0; kst < 4; ++kst) {
-      const uint32_t* pp = pk + kst * 4;
+    for (int kk = 0; kk < 2; ++kk) {
+      const int kst = kb * 2 + kk;
+      const uint32_t* pp = pb + kk * 4;
       const bf16x8 pop = __builtin_bit_cast(bf16x8, u32x4{pp[0], pp[1], pp[2], pp[3]});
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
@@ -319,48 +336,64 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       }
     }
   };
-  // Probabilities of one tile against reference m (exp2 domain): packed bf16
-  // in pk (C-element order), their sum (of the rounded values) returned.
-  auto probs = [&](const f32x16* sc, float m, uint32_t* pk) -> float {
-    const float mc = m * c;
-    float rs = 0.f;
+  // Keys of block kb of tile t past each row's limit leave the scores.
+  auto mask_blk = [&](int t, int kb, f32x16& sb) {
+    const int rel = limit - t * kAttnKeys - kb * 32 - half * 4;   // visible key offsets within the block
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][j], c, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][j + 1], c, -mc));
-        const uint32_t pb = pack_bf16x2(p0, p1);
-        pk[kb * 8 + (j >> 1)] = pb;
-        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb),
-                                             __builtin_bit_cast(bf16x2, ones_bf16x2), rs, false);
-      }
-    return rs;
+    for (int j = 0; j < 16; ++j)
+      if ((j >> 2) * 8 + (j & 3) > rel) sb[j] = -INFINITY;
   };
-  // Keys past each row's limit leave the scores (tiles from t_mask on).
-  auto mask = [&](int t, f32x16* sc) {
-    const int rel = limit - t * kAttnKeys - half * 4;   // visible key offsets within the tile
+  // Probabilities of one block against reference mr (exp2 domain), packed to
+  // bf16 pairs in pb; returns their fp32 sum.
+  auto probs_blk = [&](const f32x16& sb, float mr, uint32_t* pb) -> float {
+    const float mc = mr * c;
+    float r0 = 0.f, r1 = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (kb * 32 + (j >> 2) * 8 + (j & 3) > rel) sc[kb][j] = -INFINITY;
+    for (int j = 0; j < 16; j += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[j], c, -mc));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[j + 1], c, -mc));
+      pb[j >> 1] = pack_bf16x2(p0, p1);
+      r0 += p0;
+      r1 += p1;
+    }
+    return r0 + r1;
   };
-  // Softmax of one tile's (masked) scores: running max, probabilities into
-  // pk with the current reference, and the rare raise of the reference.
-  auto softmax = [&](f32x16* sc, uint32_t* pk) {
-    float mx = -INFINITY;
+  // Online softmax of one 32-key block with a lazy reference: probabilities
+  // against the current reference; if some row's probability exceeds 2^8
+  // (its max grew by more than 8 in log2 units), the rare raise.  A raise rescales O and
+  // l, which at that point hold only terms taken with the old reference, and
+  // recomputes this block's probabilities; every other block's P has either
+  // been added to O already or is computed later.  The test reads the
+  // probabilities themselves, so the common path stays one basic block.
+  auto sm_blk = [&](const f32x16& sb, uint32_t* pb) {
+    const float mc = m_run * c;
+    float pmax = 0.f, r0 = 0.f, r1 = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[kb][j]);
-    mx = wave_half_max(mx);
-    float rs = probs(sc, m_run, pk);
-    const bool grow = mx > m_run + tau;
+    for (int j = 0; j < 16; j += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[j], c, -mc));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[j + 1], c, -mc));
+      pb[j >> 1] = pack_bf16x2(p0, p1);
+      pmax = fmaxf(pmax, fmaxf(p0, p1));
+      r0 += p0;
+      r1 += p1;
+    }
+    float rs = r0 + r1;
+    const bool grow = wave_half_max(pmax) > kGrowLimit;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // rare: raise the reference
+      // The first pass's results count as used here, so the compiler keeps
+      // that pass ahead of the branch, next to the MFMAs it overlaps, rather
+      // than sinking it into the common path (which also splits O's
+      // registers into two copies).
+      asm volatile("" ::"v"(rs));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) asm volatile("" ::"v"(pb[j]));
+      float mx = sb[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sb[j]);
+      mx = wave_half_max(mx);
       const float m_new = grow ? mx : m_run;
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-      rs = probs(sc, m_new, pk);
+      rs = probs_blk(sb, m_new, pb);
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
@@ -381,73 +414,92 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   };
 
   // Pipeline.  Tile t lives in ring stage t % 4.  Step t issues the page ids
-  // of tile t+3 and the loads of tile t+2, computes S(t) = QK(t), then the PV
-  // product of tile t-1 (whose probabilities are ready) together with the
-  // softmax of tile t, so each wave's VALU work overlaps its own MFMAs.  The
-  // barrier at the end of step t publishes tile t+1 and retires every read of
-  // tile t-1's stage, which step t+1 refills with tile t+3.  The PV product
-  // of tile t-1 reads the probability registers before the softmax of tile t
-  // overwrites them.
+  // of tile t+3 and the loads of tile t+2, then runs two halves, each one
+  // basic block in which MFMAs and the softmax VALU work are independent:
+  //   half 1: S^T block 0 of tile t, PV of block 0 of tile t-1, softmax of
+  //           block 1 of tile t-1;
+  //   half 2: S^T block 1 of tile t, PV of block 1 of tile t-1, softmax of
+  //           block 0 of tile t.
+  // The barrier at the end of step t publishes tile t+1 and retires every
+  // read of tile t-1's stage, which step t+1 refills with tile t+3.
+  // Between steps, s1 holds S^T block 1 of the last tile and pk[0..7] the
+  // probabilities of its block 0; pk[8..15] hold block 1's once computed.
   uint32_t pk[16];
   if (n_tiles > 0) {
     Pages pg0 = fetch_pages(0), pg1 = fetch_pages(1);
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
     issue_tile(0, I0{}, pg0);
     Pages pg_next = fetch_pages(2);
-    if (n_tiles > 1) issue_tile(1, I1{}, pg1);
+    if (n_pad > 1) issue_tile(1, I1{}, pg1);
     wait_tile(0);
     step_barrier();
 
-    // One pipeline step; MASKED tiles hold keys past some row's limit.
-    auto step = [&](auto stc, auto maskc, int t) {
-      constexpr int st = decltype(stc)::value;   // t % kStages
-      constexpr bool MASKED = decltype(maskc)::value;
-      const Pages pg_after = fetch_pages(t + 3);
-      if (t + 2 < n_tiles) issue_tile(t + 2, std::integral_constant<int, (st + 2) % kStages>{}, pg_next);
-      pg_next = pg_after;
-      f32x16 sc[2];
-      qk(stc, sc);
-      if constexpr (MASKED) mask(t, sc);
-      pv(std::integral_constant<int, (st + kStages - 1) % kStages>{}, pk);
-      softmax(sc, pk);
-      wait_tile(t + 1);
-      step_barrier();
-    };
-    auto step_any = [&](auto maskc, int t) {
-      switch (t & 3) {
-        case 0: step(I0{}, maskc, t); break;
-        case 1: step(I1{}, maskc, t); break;
-        case 2: step(I2{}, maskc, t); break;
-        default: step(I3{}, maskc, t); break;
-      }
-    };
-
-    // Step 0: no previous PV product to overlap.
+    f32x16 s1;
+    // Step 0: no previous tile.
     {
       const Pages pg_after = fetch_pages(3);
-      if (2 < n_tiles) issue_tile(2, I2{}, pg_next);
+      if (2 < n_pad) issue_tile(2, I2{}, pg_next);
       pg_next = pg_after;
-      f32x16 sc[2];
-      qk(I0{}, sc);
-      if (t_mask == 0) mask(0, sc);
-      softmax(sc, pk);
+      f32x16 s0 = qk_blk(I0{}, I0{});
+      s1 = qk_blk(I0{}, I1{});
+      if (t_mask == 0) {
+        mask_blk(0, 0, s0);
+        mask_blk(0, 1, s1);
+      }
+      sm_blk(s0, pk);
       wait_tile(1);
       step_barrier();
     }
+
+    // Step t >= 1; MASKED tiles hold keys past some row's limit.
+    auto step = [&](auto stc, auto maskc, int t) {
+      constexpr int st = decltype(stc)::value;   // t % kStages
+      constexpr bool MASKED = decltype(maskc)::value;
+      using SP = std::integral_constant<int, (st + kStages - 1) % kStages>;   // stage of tile t-1
+      const Pages pg_after = fetch_pages(t + 3);
+      if (t + 2 < n_pad) issue_tile(t + 2, std::integral_constant<int, (st + 2) % kStages>{}, pg_next);
+      pg_next = pg_after;
+      f32x16 s0 = qk_blk(stc, I0{});
+      pv_blk(SP{}, I0{}, pk);
+      sm_blk(s1, pk + 8);
+      s1 = qk_blk(stc, I1{});
+      if constexpr (MASKED) mask_blk(t, 0, s0);
+      pv_blk(SP{}, I1{}, pk + 8);
+      sm_blk(s0, pk);
+      if constexpr (MASKED) mask_blk(t, 1, s1);
+      wait_tile(t + 1);
+      step_barrier();
+    };
+    // The last tile's PV products and its block-1 softmax (stage st).
+    auto finish = [&](auto stc) {
+      pv_blk(stc, I0{}, pk);
+      sm_blk(s1, pk + 8);
+      pv_blk(stc, I1{}, pk + 8);
+    };
+
     int t = 1;
     const int t_full_end = max(1, t_mask);          // tiles [1, t_mask) need no mask
-    for (; t < t_full_end; ++t) step_any(std::false_type{}, t);
-    for (; t < n_tiles; ++t) step_any(std::true_type{}, t);
-    // The last tile's PV product.
-    switch ((n_tiles - 1) & 3) {
-      case 0: pv(I0{}, pk); break;
-      case 1: pv(I1{}, pk); break;
-      case 2: pv(I2{}, pk); break;
-      default: pv(I3{}, pk); break;
+    // Both loops are unrolled by the ring depth, so every stage index is a
+    // constant and each loop body is a single path.  After the first, t % 4
+    // == 1; the second runs the remaining tiles (a few fully visible ones,
+    // which the mask leaves unchanged, then the diagonal) up to n_pad, and
+    // its padding tiles are fully masked.  The last tile, n_pad - 1, is then
+    // always in stage 0.
+    for (; t + 3 < t_full_end; t += 4) {
+      step(I1{}, std::false_type{}, t);
+      step(I2{}, std::false_type{}, t + 1);
+      step(I3{}, std::false_type{}, t + 2);
+      step(I0{}, std::false_type{}, t + 3);
     }
+    for (; t < n_pad; t += 4) {
+      step(I1{}, std::true_type{}, t);
+      step(I2{}, std::true_type{}, t + 1);
+      step(I3{}, std::true_type{}, t + 2);
+      step(I0{}, std::true_type{}, t + 3);
+    }
+    // The last tile's PV products and its block-1 softmax.
+    pv_blk(I0{}, I0{}, pk);
+    sm_blk(s1, pk + 8);
+    pv_blk(I0{}, I1{}, pk + 8);
   }
 
   // Epilogue: O = O^T / l.  Lane (col, half) holds d = 32*db + 8*(j/4) + 4*half + j%4.
