@@ -237,9 +237,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   };
   const int page0 = ptab[0];
   const bool page0_ok = page0 >= 0 && page0 < a.num_pages;
+  // Per-lane part of a load address when a whole tile lies in one page.
+  uint32_t ld_const[LOADS];
+#pragma unroll
+  for (int u = 0; u < LOADS; ++u) ld_const[u] = (uint32_t)ld_row[u] * tok_stride + ld_lane[u];
   auto issue_tile = [&](int t, auto stc, const Pages& pg) {
     unsigned char* kd = kbuf(stc);
     unsigned char* vd = vbuf(stc);
+    // Common case (a tile within one page): every key of the tile is real
+    // and its page id valid, so each address is a wave-uniform base plus a
+    // per-lane constant.
+    if (PAGE_PER_TILE && (t + 1) * kAttnKeys <= s.kv_len && pg.p[0] >= 0 && pg.p[0] < a.num_pages) {
+      const uint64_t base =
+          (((uint64_t)pg.p[0] << shift) | (uint32_t)((t * kAttnKeys) & ps_mask)) * tok_stride;
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) {
+        __builtin_amdgcn_global_load_lds(a.k_pool + (int64_t)(base + ld_const[u]),
+            (__attribute__((address_space(3))) void*)&kd[(u * kWaves + wave) * 1024], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(a.v_pool + (int64_t)(base + ld_const[u]),
+            (__attribute__((address_space(3))) void*)&vd[(u * kWaves + wave) * 1024], 16, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int key = t * kAttnKeys + ld_row[u];
@@ -289,11 +308,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const float c = a.scale_log2;
-  // Rescale threshold: the running max is only raised when a row's max grows
-  // by more than 8 in log2 units, i.e. when some probability against the
-  // current reference exceeds 2^8; so O and l are rescaled rarely (the result
-  // is the same softmax with another reference).
-  constexpr float kGrowLimit = 256.f;
+  // Rescale threshold: the running max is only raised when a lane's sum of
+  // one block's probabilities against the current reference exceeds 2^32, so
+  // O and l are rescaled rarely (the result is the same softmax with another
+  // reference).
+  constexpr float kSumLimit = 4294967296.f;
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -359,27 +378,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     return r0 + r1;
   };
   // Online softmax of one 32-key block with a lazy reference: probabilities
-  // against the current reference; if some row's probability exceeds 2^8
-  // (its max grew by more than 8 in log2 units), the rare raise.  A raise rescales O and
-  // l, which at that point hold only terms taken with the old reference, and
-  // recomputes this block's probabilities; every other block's P has either
-  // been added to O already or is computed later.  The test reads the
-  // probabilities themselves, so the common path stays one basic block.
+  // against the current reference; if some lane's block sum exceeds 2^32 (or
+  // is not finite), the rare raise of that wave's references to their rows'
+  // maxima.  A raise rescales O and l, which at that point hold only terms
+  // taken with the old reference, and recomputes this block's probabilities;
+  // every other block's P has either been added to O already or is computed
+  // later.  The test reads the sums themselves, so the common path stays one
+  // basic block.  Between raises every probability stays below 2^32, far
+  // from fp32 overflow in O and l.
   auto sm_blk = [&](const f32x16& sb, uint32_t* pb) {
     const float mc = m_run * c;
-    float pmax = 0.f, r0 = 0.f, r1 = 0.f;
+    float r0 = 0.f, r1 = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; j += 2) {
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[j], c, -mc));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[j + 1], c, -mc));
       pb[j >> 1] = pack_bf16x2(p0, p1);
-      pmax = fmaxf(pmax, fmaxf(p0, p1));
       r0 += p0;
       r1 += p1;
     }
     float rs = r0 + r1;
-    const bool grow = wave_half_max(pmax) > kGrowLimit;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // rare: raise the reference
+    if (__builtin_amdgcn_ballot_w64(!(rs <= kSumLimit)) != 0) {   // rare: raise the references
       // The first pass's results count as used here, so the compiler keeps
       // that pass ahead of the branch, next to the MFMAs it overlaps, rather
       // than sinking it into the common path (which also splits O's
@@ -391,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sb[j]);
       mx = wave_half_max(mx);
-      const float m_new = grow ? mx : m_run;
+      const float m_new = fmaxf(m_run, mx);   // rows whose max did not grow keep theirs
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
       rs = probs_blk(sb, m_new, pb);
       l_run *= alpha;
