@@ -113,7 +113,7 @@ def cpu_baseline(w, meta_lists, q_loc, k_seq, v_seq, n_rows: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py runs on one GPU only: the exchange between GPUs is not implemented (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:

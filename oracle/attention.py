@@ -14,7 +14,7 @@ KV head serves a contiguous group of query heads; scale head_size**-0.5);
 [P2] (AllGather-KV: local Q against global K/V, the pad is a strict suffix of
 K/V that no query consumes).
 
-Readings (the design doc lists them): causal alignment is bottom-right (the only
+Readings: causal alignment is bottom-right (the only
 alignment under which the ranks' shares add up to full-sequence causal
 attention; tests check that union by brute force); AllGather-KV query rows at
 or past ``q_real`` are written as zeros.

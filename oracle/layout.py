@@ -9,7 +9,7 @@ zero-padded to max_rank_len, concatenated rank after rank, pads stripped),
 cp_reverse_index order) and ``materialize_full_kv`` (write the full-sequence
 K/V rows to the cache slots of the extend tokens).
 
-Readings (the design doc lists them): the KV pool is ``[num_pages, page_size, ...]``
+Readings: the KV pool is ``[num_pages, page_size, ...]``
 and the page table is CSR (``page_indptr[bs+1]``, ``page_indices``); extend
 token t of sequence b goes to sequence position prefix_b + t.
 """

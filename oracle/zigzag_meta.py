@@ -5,7 +5,7 @@ docstring, ``ZigzagCPStrategy.can_apply`` for validity, and
 ``ZigzagCPStrategy.build_metadata`` for every list.  Written from the
 definitions, step by step, in the pages' names.
 
-Readings where the page leaves a step open (all listed in the design doc):
+Readings where the page leaves a step open:
   * ``num_tokens`` smaller than the sum of extend lengths is rejected (the page
     only handles a surplus, which goes to the last sequence).
   * Validation follows ``can_apply``: cp_size >= 2, num_tokens >= 2*cp_size,
