@@ -54,6 +54,28 @@ __global__ __launch_bounds__(kCopyThreads) void rerange_kernel(
   }
 }
 
+// Rows whose size is not a multiple of 16 bytes (positions, narrow
+// per-token tensors): the same chunk/part split, copied in elements of T,
+// the widest power of two up to 8 bytes that divides the row size, so every
+// access stays aligned.  These tensors are small; one element per lane and
+// step is enough.
+template <typename T>
+__global__ __launch_bounds__(kCopyThreads) void rerange_narrow_kernel(
+    const Chunk* __restrict__ chunks, int32_t parts_per_chunk, int32_t forward,
+    const unsigned char* __restrict__ src, unsigned char* __restrict__ dst, int64_t row_bytes) {
+  const int c = blockIdx.x / parts_per_chunk;
+  const int part = blockIdx.x - c * parts_per_chunk;
+  const Chunk ch = chunks[c];
+  const int64_t nbytes = (int64_t)ch.n_rows * row_bytes;
+  const int64_t start = (int64_t)part * kCopyBytesPerWG;
+  if (start >= nbytes) return;
+  const int64_t g_off = (int64_t)ch.g_row * row_bytes, o_off = (int64_t)ch.o_row * row_bytes;
+  const T* s = reinterpret_cast<const T*>(src + (forward ? g_off : o_off) + start);
+  T* d = reinterpret_cast<T*>(dst + (forward ? o_off : g_off) + start);
+  const int64_t n = (nbytes - start < kCopyBytesPerWG ? nbytes - start : kCopyBytesPerWG) / (int64_t)sizeof(T);
+  for (int64_t i = threadIdx.x; i < n; i += kCopyThreads) d[i] = s[i];
+}
+
 constexpr int kScatterRows = 16;  // token rows per workgroup
 
 // One workgroup copies rows [part*16, part*16+16) of chunk c, for K and V.
@@ -123,9 +145,7 @@ extern "C" int cp_zigzag_rerange(const void* d_blob, const cp_meta_t* meta, int3
     return set_error(CP_ERR_INVALID_ARG, "metadata is not zigzag metadata of this version");
   if (direction != CP_RERANGE_GATHERED_TO_ORIG && direction != CP_RERANGE_ORIG_TO_GATHERED)
     return set_error(CP_ERR_INVALID_ARG, "direction=%d", direction);
-  if (row_bytes <= 0 || row_bytes % 16 != 0)
-    return set_error(CP_ERR_UNSUPPORTED, "row_bytes=%lld must be a positive multiple of 16",
-                     (long long)row_bytes);
+  if (row_bytes <= 0) return set_error(CP_ERR_INVALID_ARG, "row_bytes=%lld must be positive", (long long)row_bytes);
   if (!src || !dst) return set_error(CP_ERR_INVALID_ARG, "src or dst is NULL");
   if (!aligned16(src) || !aligned16(dst))
     return set_error(CP_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
@@ -136,9 +156,20 @@ extern "C" int cp_zigzag_rerange(const void* d_blob, const cp_meta_t* meta, int3
     return set_error(CP_ERR_OVERFLOW, "rerange grid too large");
   if (grid == 0) return CP_OK;
   const Chunk* chunks = reinterpret_cast<const Chunk*>(static_cast<const char*>(d_blob) + meta->off_chunks);
-  hipLaunchKernelGGL(rerange_kernel, dim3((unsigned)grid), dim3(kCopyThreads), 0, stream, chunks,
-                     (int32_t)parts, (int32_t)(direction == CP_RERANGE_GATHERED_TO_ORIG),
-                     static_cast<const unsigned char*>(src), static_cast<unsigned char*>(dst), row_bytes);
+  const int32_t fwd = direction == CP_RERANGE_GATHERED_TO_ORIG;
+  const unsigned char* sp = static_cast<const unsigned char*>(src);
+  unsigned char* dp = static_cast<unsigned char*>(dst);
+  const dim3 g((unsigned)grid), b(kCopyThreads);
+  if (row_bytes % 16 == 0)
+    hipLaunchKernelGGL(rerange_kernel, g, b, 0, stream, chunks, (int32_t)parts, fwd, sp, dp, row_bytes);
+  else if (row_bytes % 8 == 0)
+    hipLaunchKernelGGL(rerange_narrow_kernel<uint64_t>, g, b, 0, stream, chunks, (int32_t)parts, fwd, sp, dp, row_bytes);
+  else if (row_bytes % 4 == 0)
+    hipLaunchKernelGGL(rerange_narrow_kernel<uint32_t>, g, b, 0, stream, chunks, (int32_t)parts, fwd, sp, dp, row_bytes);
+  else if (row_bytes % 2 == 0)
+    hipLaunchKernelGGL(rerange_narrow_kernel<uint16_t>, g, b, 0, stream, chunks, (int32_t)parts, fwd, sp, dp, row_bytes);
+  else
+    hipLaunchKernelGGL(rerange_narrow_kernel<uint8_t>, g, b, 0, stream, chunks, (int32_t)parts, fwd, sp, dp, row_bytes);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(CP_ERR_HIP, "rerange launch: %s", hipGetErrorString(e));
   return CP_OK;

@@ -156,10 +156,13 @@ int cp_allgather_meta_build(int32_t q_total, int32_t q_real, int32_t kv_len,
  *   CP_RERANGE_ORIG_TO_GATHERED: src [total_seq_lens, row] -> dst
  *     [cp*max_rank_len, row]; every rank's shard lands at its slot, pad rows
  *     of dst are left untouched.
- *   row_bytes must be a positive multiple of 16.
- * Errors: bad direction, meta kind not zigzag, row_bytes not a multiple of 16,
- * NULL or misaligned pointers -> CP_ERR_INVALID_ARG / CP_ERR_UNSUPPORTED;
- * launch failure -> CP_ERR_HIP.
+ *   row_bytes: any positive row size.  Multiples of 16 (K/V rows, hidden
+ *   states) move as 16-byte vectors; other sizes (int32/int64 positions,
+ *   narrow per-token tensors) in elements of the widest power of two up to
+ *   8 bytes that divides row_bytes.  src and dst must be 16-byte aligned and
+ *   must not overlap.
+ * Errors: bad direction, meta kind not zigzag, row_bytes <= 0, NULL or
+ * misaligned pointers -> CP_ERR_INVALID_ARG; launch failure -> CP_ERR_HIP.
  */
 int cp_zigzag_rerange(const void* d_blob, const cp_meta_t* meta, int32_t direction,
                       const void* src, void* dst, int64_t row_bytes, hipStream_t stream);

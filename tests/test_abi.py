@@ -219,7 +219,8 @@ def test_copy_validation_fails_closed(lib):
     m = cpa.meta_build(2, 0, [64], attn_group=8)
     ag = cpa.allgather_meta_build(64, 64, 64, 8)
     assert lib.cp_zigzag_rerange(FAKE, ctypes.byref(m.c), 2, FAKE, FAKE, 256, None) == cpa.CP_ERR_INVALID_ARG
-    assert lib.cp_zigzag_rerange(FAKE, ctypes.byref(m.c), 0, FAKE, FAKE, 12, None) == cpa.CP_ERR_UNSUPPORTED
+    assert lib.cp_zigzag_rerange(FAKE, ctypes.byref(m.c), 0, FAKE, FAKE, 0, None) == cpa.CP_ERR_INVALID_ARG
+    assert lib.cp_zigzag_rerange(FAKE, ctypes.byref(m.c), 0, FAKE, FAKE, -4, None) == cpa.CP_ERR_INVALID_ARG
     assert lib.cp_zigzag_rerange(FAKE, ctypes.byref(m.c), 0, FAKE_MISALIGNED, FAKE, 256, None) == cpa.CP_ERR_INVALID_ARG
     assert lib.cp_zigzag_rerange(FAKE, ctypes.byref(ag.c), 0, FAKE, FAKE, 256, None) == cpa.CP_ERR_INVALID_ARG
     sc = lib.cp_kv_scatter

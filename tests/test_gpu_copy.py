@@ -49,6 +49,57 @@ def test_rerange_both_directions_bit_exact(cp, lens, row_bytes):
     assert np.array_equal(dst2.cpu().numpy(), layout.rerange_inverse(x, mo, blank))
 
 
+def _narrow_variants():
+    rng = random.Random(23)
+    out = [(4, [1024, 777, 4093], rb) for rb in (1, 2, 3, 4, 6, 8, 12, 24, 40)]
+    for _ in range(6):
+        cp = rng.choice([2, 3, 5, 8])
+        lens = [rng.randint(2 * cp, 2 * cp * 40 + 13) for _ in range(rng.randint(1, 3))]
+        out.append((cp, lens, rng.choice([1, 4, 8, 20])))
+    return out
+
+
+@pytest.mark.parametrize("cp,lens,row_bytes", _narrow_variants())
+def test_rerange_narrow_rows_bit_exact(cp, lens, row_bytes):
+    """Rows that are not a multiple of 16 bytes (positions, narrow per-token
+    tensors), uneven blocks and several sequences, every rank, both directions."""
+    total = sum(lens)
+    x = np.random.default_rng(row_bytes).integers(0, 256, size=(total, row_bytes), dtype=np.uint8)
+    for rank in range(cp):
+        mo = zigzag_meta.build(cp, rank, total, extend_lens=lens)
+        meta = cpa.meta_build(cp, rank, lens, device="cuda")
+        g_ref = layout.gathered_buffer(x, mo, pad_value=0xA5)
+        dst = torch.full((total, row_bytes), 0x5A, dtype=torch.uint8, device="cuda")
+        cpa.zigzag_rerange(meta, torch.from_numpy(g_ref).cuda(), dst, cpa.GATHERED_TO_ORIG)
+        torch.cuda.synchronize()
+        assert np.array_equal(dst.cpu().numpy(), layout.rerange(g_ref, mo))
+        blank = np.full_like(g_ref, 0x3C)
+        dst2 = torch.from_numpy(blank).cuda()
+        cpa.zigzag_rerange(meta, torch.from_numpy(x).cuda(), dst2, cpa.ORIG_TO_GATHERED)
+        torch.cuda.synchronize()
+        assert np.array_equal(dst2.cpu().numpy(), layout.rerange_inverse(x, mo, blank))
+
+
+@pytest.mark.parametrize("dtype", ["int32", "int64"])
+def test_rerange_positions(dtype):
+    """Positions of the varlen workload (one int per token) through the
+    zigzag layout and back: the gathered shards hold each rank's positions."""
+    wl = synth.WORKLOADS["varlen_cp4_bs8"]
+    lens = synth.sequence_lengths(wl)
+    total = sum(lens)
+    pos = np.concatenate([np.arange(n) for n in lens]).astype(dtype)
+    mo = zigzag_meta.build(wl.cp_size, 0, total, extend_lens=lens)
+    meta = cpa.meta_build(wl.cp_size, 0, lens, device="cuda")
+    tdt = getattr(torch, dtype)
+    g = torch.full((wl.cp_size * meta.max_rank_len,), -1, dtype=tdt, device="cuda")
+    cpa.zigzag_rerange(meta, torch.from_numpy(pos).cuda(), g, cpa.ORIG_TO_GATHERED)
+    back = torch.empty(total, dtype=tdt, device="cuda")
+    cpa.zigzag_rerange(meta, g, back, cpa.GATHERED_TO_ORIG)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.cpu().numpy(), layout.rerange_inverse(pos, mo, np.full(g.shape, -1, dtype=dtype)))
+    assert np.array_equal(back.cpu().numpy(), pos)
+
+
 def test_rerange_config4_kv_full_size():
     """K and V of the long-context workload: [131072, 8, 128] bf16 each."""
     w = synth.WORKLOADS["long_cp8_s131072_r3"]
