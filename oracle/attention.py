@@ -132,6 +132,34 @@ def allgather_kv(q_local, k_global, v_global, q_real: int, kv_real: int,
     return out
 
 
+def allgather_kv_packed(q_local, k_global, v_global, doc_cu: Sequence[int], q_start: int,
+                        scale: float, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """AllGather-KV over a packed global sequence ([P2]: the query ranges of a
+    rank's local slice, one per document it covers, and the local query
+    boundaries remapped from the global ones).
+
+    The global sequence packs documents back to back: document b holds global
+    rows doc_cu[b] .. doc_cu[b+1]-1 (doc_cu[0] = 0) and rows at or past
+    doc_cu[-1] are the pad suffix.  Local query row i is global row
+    q_start + i; it attends, with no causal mask, to the K/V rows of its own
+    document, and its output is zero if it lies in the pad suffix.
+    ``rows`` restricts the output to the listed local rows."""
+    q_local = _f64(q_local)
+    n = q_local.shape[0]
+    rows = list(range(n)) if rows is None else list(rows)
+    out = np.zeros((len(rows),) + q_local.shape[1:], dtype=np.float64)
+    cu = [int(c) for c in doc_cu]
+    for b in range(len(cu) - 1):
+        lo, hi = cu[b], cu[b + 1]
+        sel = [i for i, r in enumerate(rows) if lo <= q_start + r < hi]
+        if not sel:
+            continue
+        local = [rows[i] for i in sel]
+        out[sel] = attention_rows(q_local[local], local, k_global[lo:hi], v_global[lo:hi],
+                                  q_len=len(local), kv_len=hi - lo, causal=False, scale=scale)
+    return out
+
+
 def default_scale(d: int) -> float:
     """[P4]: softmax scale is head_size ** -0.5."""
     return 1.0 / math.sqrt(d)

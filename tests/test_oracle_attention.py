@@ -218,3 +218,83 @@ def test_useful_pairs_closed_forms():
     assert oatt.useful_pairs(5, 5, True) == 15
     assert oatt.useful_pairs(4, 10, True) == sum(range(7, 11))
     assert oatt.useful_pairs(8192, 30000, False) == 8192 * 30000
+
+
+def _packed_case(rng, lens, pad, hq, hkv, d=8):
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    total = cu[-1] + pad
+    qg = rng.standard_normal((total, hq, d))
+    k = rng.standard_normal((total, hkv, d))
+    v = rng.standard_normal((total, hkv, d))
+    k[cu[-1]:] = np.nan      # the pad suffix is never consumed
+    v[cu[-1]:] = np.nan
+    return cu, qg, k, v
+
+
+def test_allgather_packed_matches_sdpa_block_diagonal_float64():
+    """Library special case: attention over the whole packed sequence with a
+    block-diagonal mask (a row sees exactly its own document's keys), by
+    torch's scaled_dot_product_attention in float64, restricted to each
+    rank's local slice of rows."""
+    rng = np.random.default_rng(11)
+    for lens, pad, hq, hkv, a in [([5, 9, 3, 7], 8, 4, 2, 4), ([20], 4, 2, 1, 2), ([1, 1, 6, 2, 2], 0, 6, 3, 3)]:
+        cu, qg, k, v = _packed_case(rng, lens, pad, hq, hkv)
+        total = qg.shape[0]
+        real = cu[-1]
+        doc = np.searchsorted(np.asarray(cu), np.arange(real), side="right") - 1
+        g = hq // hkv
+        tq = torch.from_numpy(qg[:real]).permute(1, 0, 2)
+        tk = torch.from_numpy(np.repeat(k[:real], g, axis=1)).permute(1, 0, 2)
+        tv = torch.from_numpy(np.repeat(v[:real], g, axis=1)).permute(1, 0, 2)
+        mask = torch.from_numpy(doc[:, None] == doc[None, :])
+        full = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, attn_mask=mask, scale=0.41).permute(1, 0, 2).numpy()
+        share = -(-total // a)
+        for r in range(a):
+            q0, q1 = r * share, min(total, (r + 1) * share)
+            got = oatt.allgather_kv_packed(qg[q0:q1], k, v, cu, q0, scale=0.41)
+            assert not np.any(np.isnan(got))
+            for i in range(q1 - q0):
+                if q0 + i < real:
+                    assert np.max(np.abs(got[i] - full[q0 + i])) < 1e-12
+                else:
+                    assert np.all(got[i] == 0)
+
+
+def test_allgather_packed_closed_forms_and_special_cases():
+    rng = np.random.default_rng(12)
+    # documents of one token: each row sees only itself, so O = that row's V
+    cu, qg, k, v = _packed_case(rng, [1] * 6, 2, 4, 2)
+    o = oatt.allgather_kv_packed(qg[2:8], k, v, cu, 2, scale=0.5)
+    g = 2
+    for i in range(4):
+        for h in range(4):
+            assert np.allclose(o[i, h], v[2 + i, h // g], atol=1e-15, rtol=0)
+    assert np.all(o[4:] == 0)
+    # one document starting at row 0 is the single-range AllGather-KV share
+    cu, qg, k, v = _packed_case(rng, [30], 6, 4, 4)
+    a = oatt.allgather_kv_packed(qg[10:36], k, v, cu, 10, scale=0.3)
+    b = oatt.allgather_kv(qg[10:36], k, v, q_real=20, kv_real=30, scale=0.3)
+    assert np.max(np.abs(a - b)) < 1e-14
+    # row sampling gives the same rows
+    sub = oatt.allgather_kv_packed(qg[10:36], k, v, cu, 10, scale=0.3, rows=[25, 3, 19])
+    assert np.array_equal(sub, a[[25, 3, 19]])
+
+
+def test_allgather_packed_document_order_invariance():
+    """Moving a document elsewhere in the packing moves its outputs with it and
+    changes nothing else (documents do not see each other)."""
+    rng = np.random.default_rng(13)
+    lens = [4, 7, 5]
+    cu, qg, k, v = _packed_case(rng, lens, 0, 2, 1)
+    o = oatt.allgather_kv_packed(qg, k, v, cu, 0, scale=0.7)
+    order = [2, 0, 1]
+    segs = [slice(cu[b], cu[b + 1]) for b in order]
+    q2, k2, v2 = (np.concatenate([x[s] for s in segs]) for x in (qg, k, v))
+    cu2 = [0]
+    for b in order:
+        cu2.append(cu2[-1] + lens[b])
+    o2 = oatt.allgather_kv_packed(q2, k2, v2, cu2, 0, scale=0.7)
+    assert np.max(np.abs(o2 - np.concatenate([o[s] for s in segs]))) < 1e-14
