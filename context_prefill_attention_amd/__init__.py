@@ -78,13 +78,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P = ctypes.POINTER
     lib.cp_meta_build.argtypes = [_i32, _i32, _i32, P(_i32), P(_i32), _i64, _i32, _vp, _i64, P(CMeta)]
     lib.cp_allgather_meta_build.argtypes = [_i32, _i32, _i32, _i32, _vp, _i64, P(CMeta)]
+    lib.cp_allgather_packed_meta_build.argtypes = [_i32, P(_i32), _i32, _i32, _i32, _vp, _i64, P(CMeta)]
     lib.cp_zigzag_rerange.argtypes = [_vp, P(CMeta), _i32, _vp, _vp, _i64, _vp]
     lib.cp_kv_scatter.argtypes = [_vp, P(CMeta), _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                   _vp, _vp, _vp]
     lib.cp_prefill_attn.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, ctypes.c_float, _vp,
                                     P(CMeta), _i32, _i32, _vp, _vp, _vp]
-    for fn in ("cp_meta_build", "cp_allgather_meta_build", "cp_zigzag_rerange", "cp_kv_scatter",
-               "cp_prefill_attn"):
+    for fn in ("cp_meta_build", "cp_allgather_meta_build", "cp_allgather_packed_meta_build",
+               "cp_zigzag_rerange", "cp_kv_scatter", "cp_prefill_attn"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.cp_last_error.restype = ctypes.c_char_p
     lib.cp_last_error.argtypes = []
@@ -189,6 +190,26 @@ def allgather_meta_build(q_total: int, q_real: int, kv_len: int, attn_group: int
     blob = np.zeros(cm.blob_bytes, dtype=np.uint8)
     _check(lib.cp_allgather_meta_build(q_total, q_real, kv_len, attn_group, blob.ctypes.data,
                                        blob.size, ctypes.byref(cm)))
+    m = Meta(cm, blob)
+    return m.to_device(device) if device is not None else m
+
+
+def allgather_packed_meta_build(doc_cu, q_start: int, q_total: int, attn_group: int,
+                                device=None) -> Meta:
+    """``cp_allgather_packed_meta_build``: metadata of the non-causal
+    AllGather-KV share of a packed global sequence (document boundaries
+    ``doc_cu``; local query rows are global rows [q_start, q_start+q_total))."""
+    lib = load_library()
+    cu = np.ascontiguousarray(np.asarray(doc_cu, dtype=np.int32))
+    if cu.ndim != 1 or cu.size < 2:
+        raise CpError(CP_ERR_INVALID_ARG, "doc_cu must be 1-D with n_docs+1 >= 2 entries")
+    cup = cu.ctypes.data_as(ctypes.POINTER(_i32))
+    cm = CMeta()
+    _check(lib.cp_allgather_packed_meta_build(cu.size - 1, cup, q_start, q_total, attn_group,
+                                              None, 0, ctypes.byref(cm)))
+    blob = np.zeros(cm.blob_bytes, dtype=np.uint8)
+    _check(lib.cp_allgather_packed_meta_build(cu.size - 1, cup, q_start, q_total, attn_group,
+                                              blob.ctypes.data, blob.size, ctypes.byref(cm)))
     m = Meta(cm, blob)
     return m.to_device(device) if device is not None else m
 

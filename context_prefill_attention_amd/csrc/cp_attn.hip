@@ -2,8 +2,9 @@
 //
 // One launch covers every segment of a metadata blob: both zigzag halves of
 // every sequence (causal, bottom-right aligned: row i of a q_len-row half
-// sees key j <= i + kv_len - q_len) or the one AllGather-KV slice
-// (non-causal, keys [0, kv_len) of the global K/V).  Sources: sglang zigzag.py
+// sees key j <= i + kv_len - q_len) or the AllGather-KV slice (non-causal,
+// each local query row against the keys of its own document of the ordered
+// global K/V).  Sources: sglang zigzag.py
 // source page (run_attention: the prev and next halves with their own
 // cu_seqlens_q and kv_len; build_metadata: kv_len_prev/next); the AITer GQA
 // report (KV head of query head h is h / (H_q/H_kv), scale 1/sqrt(D)); the
@@ -206,6 +207,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   const int shift = a.page_shift;
   const int ps_mask = (1 << shift) - 1;
   const uint32_t tok_stride = (uint32_t)h_kv * ROW_BYTES;
+  // Key j of the segment is position kv0 + j of its page-table row (kv0 > 0
+  // for all but the first document of a packed AllGather-KV slice).  When kv0
+  // is not a multiple of the tile size, a tile may straddle two pages.
+  const int kv0 = s.kv_start;
+  const bool straddle = (kv0 & (kAttnKeys - 1)) != 0;
+  const int n_entries = a.indptr[s.page_row + 1] - a.indptr[s.page_row];
   int ld_row[LOADS];
   uint32_t ld_lane[LOADS];   // chunk offset from the head-0 start of the lane's token row
 #pragma unroll
@@ -221,16 +228,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   // the sequence (always real and finite) and masked out of the scores.  The
   // per-wave vector-memory counts are then exact and the waits below can
   // leave the younger tiles in flight.
-  struct Pages { int p[PAGE_PER_TILE ? 1 : LOADS]; };
+  // With pages of >= 64 keys: the page of the tile's first key and, if the
+  // tile may straddle a page boundary, the next one.
+  struct Pages { int p[PAGE_PER_TILE ? 2 : LOADS]; };
   auto fetch_pages = [&](int t) -> Pages {
     Pages pg;
     if constexpr (PAGE_PER_TILE) {
-      pg.p[0] = ptab[(min(t, n_tiles - 1) * kAttnKeys) >> shift];
+      const int e0 = (kv0 + min(t, n_tiles - 1) * kAttnKeys) >> shift;
+      pg.p[0] = ptab[e0];
+      pg.p[1] = straddle ? ptab[min(e0 + 1, n_entries - 1)] : pg.p[0];
     } else {
 #pragma unroll
       for (int u = 0; u < LOADS; ++u) {
-        const int key = min(t * kAttnKeys + ld_row[u], s.kv_len - 1);
-        pg.p[u] = ptab[key >> shift];
+        const int key = max(0, min(t * kAttnKeys + ld_row[u], s.kv_len - 1));
+        pg.p[u] = ptab[(kv0 + key) >> shift];
       }
     }
     return pg;
@@ -247,9 +258,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     // Common case (a tile within one page): every key of the tile is real
     // and its page id valid, so each address is a wave-uniform base plus a
     // per-lane constant.
-    if (PAGE_PER_TILE && (t + 1) * kAttnKeys <= s.kv_len && pg.p[0] >= 0 && pg.p[0] < a.num_pages) {
+    const int first = kv0 + t * kAttnKeys;   // page-table position of the tile's key 0
+    if (PAGE_PER_TILE && (t + 1) * kAttnKeys <= s.kv_len && pg.p[0] >= 0 && pg.p[0] < a.num_pages &&
+        (first & ps_mask) + kAttnKeys <= ps_mask + 1) {
       const uint64_t base =
-          (((uint64_t)pg.p[0] << shift) | (uint32_t)((t * kAttnKeys) & ps_mask)) * tok_stride;
+          (((uint64_t)pg.p[0] << shift) | (uint32_t)(first & ps_mask)) * tok_stride;
 #pragma unroll
       for (int u = 0; u < LOADS; ++u) {
         __builtin_amdgcn_global_load_lds(a.k_pool + (int64_t)(base + ld_const[u]),
@@ -262,9 +275,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int key = t * kAttnKeys + ld_row[u];
-      const int page = PAGE_PER_TILE ? pg.p[0] : pg.p[u];
+      const int pos = kv0 + key;
+      int page;
+      if constexpr (PAGE_PER_TILE) page = (pos >> shift) == (first >> shift) ? pg.p[0] : pg.p[1];
+      else page = pg.p[u];
       const bool ok = key < s.kv_len && page >= 0 && page < a.num_pages;
-      const int64_t tok = ok ? ((int64_t)page << shift | (key & ps_mask))
+      const int64_t tok = ok ? ((int64_t)page << shift | (pos & ps_mask))
                              : (page0_ok ? (int64_t)page0 << shift : 0);
       const int64_t off = tok * tok_stride + ld_lane[u];
       __builtin_amdgcn_global_load_lds(a.k_pool + off,

@@ -20,7 +20,8 @@ struct Chunk {
 static_assert(sizeof(Chunk) == 32, "Chunk layout");
 
 // One attention segment: q_len query rows of one zigzag half of one
-// sequence (or the AllGather-KV slice) against that sequence's first kv_len keys.
+// sequence (or of one document of the AllGather-KV slice) against kv_len
+// keys of that sequence, starting at key kv_start of its page-table row.
 struct Seg {
   int32_t q_row0;      // first local row in Q/O
   int32_t q_len;       // rows that attend
@@ -29,7 +30,7 @@ struct Seg {
   int32_t causal_off;  // kv_len - q_len: row i sees keys j <= i + causal_off
   int32_t page_row;    // row of the CSR page table (the sequence)
   int32_t causal;      // 1: bottom-right causal mask, 0: none
-  int32_t pad;
+  int32_t kv_start;    // key j of the segment is position kv_start + j of the page-table row
 };
 static_assert(sizeof(Seg) == 32, "Seg layout");
 

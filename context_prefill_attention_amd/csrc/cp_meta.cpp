@@ -375,6 +375,83 @@ extern "C" int cp_allgather_meta_build(int32_t q_total, int32_t q_real, int32_t 
   return CP_OK;
 }
 
+extern "C" int cp_allgather_packed_meta_build(int32_t n_docs, const int32_t* doc_cu,
+                                              int32_t q_start, int32_t q_total, int32_t attn_group,
+                                              void* blob, int64_t blob_capacity, cp_meta_t* meta) {
+  clear_error();
+  if (!meta) return set_error(CP_ERR_INVALID_ARG, "meta is NULL");
+  if (n_docs < 1) return set_error(CP_ERR_INVALID_ARG, "n_docs=%d must be >= 1", n_docs);
+  if (!doc_cu) return set_error(CP_ERR_INVALID_ARG, "doc_cu is NULL");
+  if (doc_cu[0] != 0) return set_error(CP_ERR_INVALID_ARG, "doc_cu[0]=%d must be 0", doc_cu[0]);
+  for (int b = 0; b < n_docs; ++b)
+    if (doc_cu[b + 1] < doc_cu[b])
+      return set_error(CP_ERR_INVALID_ARG, "doc_cu must be non-decreasing (doc_cu[%d]=%d > doc_cu[%d]=%d)",
+                       b, doc_cu[b], b + 1, doc_cu[b + 1]);
+  if (doc_cu[n_docs] < 1) return set_error(CP_ERR_INVALID_ARG, "the packed documents are empty");
+  if (q_total < 1) return set_error(CP_ERR_INVALID_ARG, "q_total=%d must be >= 1", q_total);
+  if (q_start < 0) return set_error(CP_ERR_INVALID_ARG, "q_start=%d must be >= 0", q_start);
+  if ((int64_t)q_start + q_total > INT32_MAX)
+    return set_error(CP_ERR_OVERFLOW, "q_start + q_total exceeds int32");
+  if (int rc = check_group(attn_group, false)) return rc;
+
+  // One segment per document that meets the local rows [q_start, q_end);
+  // local rows in the pad suffix join the last segment (or form their own
+  // segment without keys if no document meets the slice).
+  const int32_t q_end = q_start + q_total, real = doc_cu[n_docs];
+  std::vector<Seg> segs;
+  int32_t max_kv = 0;
+  for (int b = 0; b < n_docs; ++b) {
+    const int32_t lo = std::max(doc_cu[b], q_start), hi = std::min(doc_cu[b + 1], q_end);
+    if (lo >= hi) continue;
+    const int32_t kv = doc_cu[b + 1] - doc_cu[b];
+    segs.push_back(Seg{lo - q_start, hi - lo, hi - lo, kv, kv - (hi - lo), 0, 0, doc_cu[b]});
+    max_kv = std::max(max_kv, kv);
+  }
+  if (q_end > real) {
+    const int32_t pad0 = std::max(real, q_start) - q_start;
+    if (!segs.empty() && segs.back().q_row0 + segs.back().q_rows == pad0)
+      segs.back().q_rows += q_total - pad0;
+    else
+      segs.push_back(Seg{pad0, 0, q_total - pad0, 0, 0, 0, 0, 0});
+  }
+  std::vector<Work> work;
+  const int q_tile = kAttnRows / attn_group;
+  build_work(segs, q_tile, work);
+
+  Layout lay;
+  cp_meta_t m;
+  std::memset(&m, 0, sizeof(m));
+  m.version = CP_META_VERSION;
+  m.kind = CP_META_ALLGATHER;
+  m.bs = 1;   // one page-table row: the ordered global K/V
+  m.attn_group = attn_group;
+  m.n_local_rows = q_total;
+  m.n_seg = (int32_t)segs.size();
+  m.n_work = (int32_t)work.size();
+  m.max_kv_len = max_kv;
+  m.q_tile = q_tile;
+  const int64_t empty = lay.take(0);
+  m.off_split_list = m.off_zigzag_index = m.off_cp_reverse_index = m.off_reverse_split_len = empty;
+  m.off_per_rank_actual_token = m.off_kv_len_prev = m.off_kv_len_next = empty;
+  m.off_q_prev = m.off_q_next = m.off_cu_seqlens_q_prev = m.off_cu_seqlens_q_next = empty;
+  m.off_prefix = m.off_extend = m.off_chunks = empty;
+  m.off_segs = lay.take((int64_t)sizeof(Seg) * segs.size());
+  m.off_work = lay.take((int64_t)sizeof(Work) * work.size());
+  m.blob_bytes = lay.cursor;
+  *meta = m;
+  if (!blob) return CP_OK;
+  if (blob_capacity < m.blob_bytes)
+    return set_error(CP_ERR_BUFFER_TOO_SMALL, "blob_capacity=%lld < blob_bytes=%lld",
+                     (long long)blob_capacity, (long long)m.blob_bytes);
+  std::memset(blob, 0, (size_t)m.blob_bytes);
+  Header h{kBlobMagic, CP_META_VERSION, CP_META_ALLGATHER, 0, m.n_seg, m.n_work, 0, 1};
+  std::memcpy(blob, &h, sizeof(h));
+  char* base = static_cast<char*>(blob);
+  std::memcpy(base + m.off_segs, segs.data(), sizeof(Seg) * segs.size());
+  std::memcpy(base + m.off_work, work.data(), sizeof(Work) * work.size());
+  return CP_OK;
+}
+
 extern "C" const char* cp_last_error(void) { return g_err; }
 
 extern "C" const char* cp_version(void) { return "cpattn 0.1 gfx950"; }

@@ -85,7 +85,7 @@ enum { CP_RERANGE_GATHERED_TO_ORIG = 0, CP_RERANGE_ORIG_TO_GATHERED = 1 };
 typedef struct cp_meta {
   int32_t version;            /* CP_META_VERSION */
   int32_t kind;               /* CP_META_ZIGZAG (causal) or CP_META_ALLGATHER */
-  int32_t cp_size, cp_rank, bs;
+  int32_t cp_size, cp_rank, bs;  /* bs: sequences = rows of the page table the attention reads (1 for AllGather-KV) */
   int32_t attn_group;         /* H_q/H_kv the work list was built for; 0 = none */
   int64_t total_seq_lens;     /* sum of extend lengths (after any surplus) */
   int32_t max_rank_len;       /* rows per rank in the all-gathered buffer */
@@ -94,7 +94,7 @@ typedef struct cp_meta {
   int32_t n_local_rows;       /* this rank's Q/O rows */
   int32_t n_chunks;           /* bs*2cp (zigzag), 0 (allgather) */
   int32_t max_chunk_rows;
-  int32_t n_seg;              /* attention segments: 2*bs (zigzag), 1 (allgather) */
+  int32_t n_seg;              /* attention segments: 2*bs (zigzag), 1 or one per document (allgather) */
   int32_t n_work;             /* attention work items */
   int32_t max_kv_len;
   int32_t q_tile;             /* query positions per work item */
@@ -147,6 +147,30 @@ int cp_allgather_meta_build(int32_t q_total, int32_t q_real, int32_t kv_len,
                             cp_meta_t* meta);
 
 /*
+ * cp_allgather_packed_meta_build -- host-only metadata of the non-causal
+ * AllGather-KV share when the global sequence packs several documents
+ * ([P2]: the query ranges of a rank's local slice and the local query
+ * boundaries remapped from the global ones).
+ *   doc_cu[n_docs+1]: document boundaries in the global sequence, exclusive
+ *     prefix sums of the real lengths (doc_cu[0] = 0, non-decreasing);
+ *     global rows at and past doc_cu[n_docs] are the pad suffix.
+ *   The local query rows are global rows [q_start, q_start + q_total).  A
+ *   local row of document b attends, with no causal mask, to K/V rows
+ *   doc_cu[b] .. doc_cu[b+1]-1 of the ordered global K/V (page-table row 0);
+ *   rows in the pad suffix are written as zeros and pad K/V rows are never
+ *   read.  One segment per document that meets the slice.
+ * The Ulysses head share is a plain smaller head count at the attention
+ * call (H_q/U query heads, their KV heads).
+ * Errors: n_docs < 1, NULL doc_cu, doc_cu[0] != 0, decreasing doc_cu, no real
+ * row, q_total < 1, q_start < 0 -> CP_ERR_INVALID_ARG; q_start + q_total
+ * beyond int32 -> CP_ERR_OVERFLOW; attn_group outside [1, 256] ->
+ * CP_ERR_UNSUPPORTED.  Blob handling as in cp_meta_build.
+ */
+int cp_allgather_packed_meta_build(int32_t n_docs, const int32_t* doc_cu, int32_t q_start,
+                                   int32_t q_total, int32_t attn_group, void* blob,
+                                   int64_t blob_capacity, cp_meta_t* meta);
+
+/*
  * cp_zigzag_rerange -- bit copy of whole rows between the all-gathered
  * layout and original token order ([P5] gather_kv_cache /
  * gather_hidden_states after _all_gather_reorganized, and shard_* for every
@@ -193,9 +217,9 @@ int cp_kv_scatter(const void* d_blob, const cp_meta_t* meta,
 
 /*
  * cp_prefill_attn -- one fused launch over every segment of the metadata:
- * both zigzag halves of every sequence (CP_META_ZIGZAG, causal) or the one
- * AllGather-KV segment (CP_META_ALLGATHER, non-causal) ([P5] run_attention,
- * [P1], [P2]).
+ * both zigzag halves of every sequence (CP_META_ZIGZAG, causal) or the
+ * AllGather-KV segments, one per document of the local slice
+ * (CP_META_ALLGATHER, non-causal) ([P5] run_attention, [P1], [P2]).
  *   For segment (half, b) with q_len rows starting at local row r0 and
  *   kv_len keys: O[r0+i, h] = softmax(scale * Q[r0+i, h] K^T + M) V over keys
  *   0..kv_len-1 of sequence b, read through the page table; KV head of query
@@ -205,8 +229,10 @@ int cp_kv_scatter(const void* d_blob, const cp_meta_t* meta,
  *     sequences, then next halves).  Fp32 accumulation, bf16 output (RNE).
  *   k_pool, v_pool, num_pages, page table: as in cp_kv_scatter.  A
  *     contiguous [S, H_kv, D] tensor is the pool with page_size dividing S
- *     and the identity page table.  Keys read through a page id outside
- *     [0, num_pages) are treated as zero rows (no out-of-bounds read).
+ *     and the identity page table.  A key whose page id lies outside
+ *     [0, num_pages) is read from the first slot of the segment's page-table
+ *     row instead: no out-of-bounds read, but such a table gives unspecified
+ *     results.
  * Requires H_q % H_kv == 0 (else CP_ERR_INVALID_ARG, [P4]), H_q/H_kv equal to
  * meta->attn_group, D in {64, 128}, page_size a power of two, scale finite
  * and > 0.

@@ -8,12 +8,13 @@ Recipe (identical everywhere):
   * float data: ``torch.Generator('cpu').manual_seed(seed)``, standard normal
     float32 drawn in the order the caller asks (Q, then K, then V), rounded to
     bfloat16 with round-to-nearest-even (torch ``.to(torch.bfloat16)``);
-  * integer structure (sequence lengths, page permutations):
+  * integer structure (sequence and document lengths, page permutations):
     ``numpy.random.default_rng(seed)``.
 
-The five workloads are the long-context, varlen and AllGather-KV shapes that
-the pages' prefill context-parallel discussions revolve around; the pages
-print no numeric inputs, so every tensor here is synthetic.
+The workloads are the long-context, varlen and AllGather-KV shapes (single
+and packed documents) that the pages' prefill context-parallel discussions
+revolve around; the pages print no numeric inputs, so every tensor here is
+synthetic.
 """
 
 from __future__ import annotations
@@ -45,6 +46,7 @@ class Workload:
     ag_degree: int = 0
     ag_rank: int = 0
     kv_heads_variants: Tuple[int, ...] = ()
+    packed_docs: Optional[Tuple[int, int]] = None   # (low, high) document lengths of a packed sequence
 
 
 WORKLOADS = {
@@ -65,6 +67,10 @@ WORKLOADS = {
         name="allgather_kv_s32768", seed=5, causal=False, h_q=32, h_kv=8, d=128, page_size=64,
         contiguous_kv=True, kv_total=32768, kv_real=30000, ag_degree=4, ag_rank=1,
         kv_heads_variants=(8, 1)),
+    "allgather_packed_s32768": Workload(
+        name="allgather_packed_s32768", seed=6, causal=False, h_q=32, h_kv=8, d=128, page_size=64,
+        contiguous_kv=True, kv_total=32768, kv_real=30000, ag_degree=4, ag_rank=1,
+        kv_heads_variants=(8, 1), packed_docs=(500, 8000)),
 }
 
 # Order used when workloads are referred to by number (1..5).
@@ -81,6 +87,22 @@ def sequence_lengths(w: Workload) -> List[int]:
     rng = np.random.default_rng(w.seed)
     u = rng.integers(lo, hi, size=w.bs, endpoint=True)
     return [int(mult * (x // mult)) for x in u]
+
+
+def packed_doc_cu(w: Workload) -> List[int]:
+    """Document boundaries of a packed global sequence: lengths uniform in
+    [low, high] (numpy default_rng(seed)) drawn until the next one would pass
+    kv_real; the last document takes the remainder, so the real rows total
+    exactly kv_real.  Returns [0, cu_1, ..., kv_real]."""
+    lo, hi = w.packed_docs
+    rng = np.random.default_rng(w.seed)
+    cu = [0]
+    while True:
+        n = int(rng.integers(lo, hi, endpoint=True))
+        if cu[-1] + n >= w.kv_real:
+            cu.append(w.kv_real)
+            return cu
+        cu.append(cu[-1] + n)
 
 
 def page_table(w: Workload, kv_lens: Sequence[int], seed_offset: int = 0):

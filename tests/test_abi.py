@@ -25,7 +25,8 @@ def lib():
 def test_library_exports_every_declared_symbol(lib):
     text = open(HEADER).read()
     names = set(re.findall(r"^\s*(?:int|const char\*)\s+(cp_\w+)\s*\(", text, flags=re.M))
-    assert {"cp_meta_build", "cp_allgather_meta_build", "cp_zigzag_rerange", "cp_kv_scatter",
+    assert {"cp_meta_build", "cp_allgather_meta_build", "cp_allgather_packed_meta_build",
+            "cp_zigzag_rerange", "cp_kv_scatter",
             "cp_prefill_attn", "cp_last_error", "cp_version"} <= names
     for n in names:
         assert hasattr(lib, n), n   # ctypes dlsym succeeds
@@ -140,6 +141,68 @@ def test_allgather_meta():
     assert work[:, 2].sum() == 100
     for s, p0, npos, nt in work:
         assert nt == (0 if p0 >= 70 else 1)
+
+
+def _expected_packed_segments(cu, q_start, q_total):
+    """Segments the packed AllGather-KV share must have, from its definition:
+    one per document that meets the local rows, pad rows joining the last one."""
+    segs = []
+    q_end = q_start + q_total
+    for b in range(len(cu) - 1):
+        lo, hi = max(cu[b], q_start), min(cu[b + 1], q_end)
+        if lo < hi:
+            kv = cu[b + 1] - cu[b]
+            segs.append([lo - q_start, hi - lo, hi - lo, kv, kv - (hi - lo), 0, 0, cu[b]])
+    if q_end > cu[-1]:
+        pad0 = max(cu[-1], q_start) - q_start
+        if segs and segs[-1][0] + segs[-1][2] == pad0:
+            segs[-1][2] += q_total - pad0
+        else:
+            segs.append([pad0, 0, q_total - pad0, 0, 0, 0, 0, 0])
+    return segs
+
+
+@pytest.mark.parametrize("cu,q_start,q_total,group", [
+    ([0, 3838, 8374, 12757, 15831, 23427, 26695, 30000], 8192, 8192, 4),
+    ([0, 3838, 8374, 12757, 15831, 23427, 26695, 30000], 24576, 8192, 32),
+    ([0, 37, 137, 142, 442, 506], 432, 144, 4),
+    ([0, 37, 137, 137, 442, 506], 0, 144, 1),      # an empty document
+    ([0, 100], 150, 50, 8),                         # a slice entirely in the pad suffix
+    ([0, 100], 0, 100, 256),
+])
+def test_allgather_packed_meta(cu, q_start, q_total, group):
+    m = cpa.allgather_packed_meta_build(cu, q_start, q_total, group)
+    assert m.kind == cpa.META_ALLGATHER and m.n_local_rows == q_total
+    segs = _unpack(m.blob, m.off_segs, m.n_seg, 8).tolist()
+    assert segs == _expected_packed_segments(cu, q_start, q_total)
+    work = _unpack(m.blob, m.off_work, m.n_work, 4)
+    tq = ROWS_PER_ITEM // group
+    assert m.q_tile == tq
+    covered = np.zeros(q_total, dtype=int)
+    for s, p0, npos, n_tiles in work:
+        sg = segs[s]
+        assert 0 < npos <= tq and p0 + npos <= sg[2]
+        covered[sg[0] + p0: sg[0] + p0 + npos] += 1
+        assert n_tiles == (0 if p0 >= sg[1] else -(-sg[3] // 64))
+    assert np.all(covered == 1)                     # every local row exactly once
+    assert list(work[:, 3]) == sorted(work[:, 3], reverse=True)
+
+
+@pytest.mark.parametrize("args,code", [
+    (([0], 0, 8, 4), cpa.CP_ERR_INVALID_ARG),
+    (([1, 9], 0, 8, 4), cpa.CP_ERR_INVALID_ARG),
+    (([0, 9, 5], 0, 8, 4), cpa.CP_ERR_INVALID_ARG),
+    (([0, 0], 0, 8, 4), cpa.CP_ERR_INVALID_ARG),
+    (([0, 9], -1, 8, 4), cpa.CP_ERR_INVALID_ARG),
+    (([0, 9], 0, 0, 4), cpa.CP_ERR_INVALID_ARG),
+    (([0, 9], 2**31 - 4, 8, 4), cpa.CP_ERR_OVERFLOW),
+    (([0, 9], 0, 8, 0), cpa.CP_ERR_UNSUPPORTED),
+    (([0, 9], 0, 8, 257), cpa.CP_ERR_UNSUPPORTED),
+])
+def test_allgather_packed_meta_rejections(args, code):
+    with pytest.raises(cpa.CpError) as ei:
+        cpa.allgather_packed_meta_build(*args)
+    assert ei.value.code == code
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -171,3 +171,77 @@ def test_mha_and_mqa_group_shapes():
         got = gc.run_attn(c)
         ref = oatt.zigzag_rank(c.q_local.cpu(), c.k_seqs, c.v_seqs, c.meta_o, c.scale)
         gc.assert_close(got, ref, f"H {h_q}/{h_kv}")
+
+
+def _packed_run(doc_cu, q_start, q_total, h_q, h_kv, d, ps, kv_total, seed, permute):
+    """Packed AllGather-KV share: global K/V [kv_total] (pad suffix NaN) as a
+    pool of pages, identity or permuted page ids; local Q = global rows
+    [q_start, q_start + q_total)."""
+    qg, kg, vg = synth.normal_bf16(seed, (kv_total, h_q, d), (kv_total, h_kv, d), (kv_total, h_kv, d))
+    real = doc_cu[-1]
+    kg[real:] = float("nan")
+    vg[real:] = float("nan")
+    q = qg[q_start:q_start + q_total].contiguous()
+    meta = cpa.allgather_packed_meta_build(doc_cu, q_start, q_total, h_q // h_kv, device="cuda")
+    npages = kv_total // ps
+    ids = np.random.default_rng(seed + 1000).permutation(npages) if permute else np.arange(npages)
+    kp = torch.empty(npages, ps, h_kv, d, dtype=torch.bfloat16)
+    vp = torch.empty_like(kp)
+    kp[torch.from_numpy(ids)] = kg.view(npages, ps, h_kv, d)   # logical page i lives at pool page ids[i]
+    vp[torch.from_numpy(ids)] = vg.view(npages, ps, h_kv, d)
+    indptr = torch.tensor([0, npages], dtype=torch.int32, device="cuda")
+    indices = torch.from_numpy(ids.astype(np.int32)).cuda()
+    out = torch.full((q_total, h_q, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    scale = 1 / math.sqrt(d)
+    cpa.prefill_attn(q.cuda(), kp.cuda(), vp.cuda(), out, meta, scale, ps, indptr, indices)
+    torch.cuda.synchronize()
+    return q, kg, vg, out, scale
+
+
+def _packed_tiny_variants():
+    cu = [0, 37, 137, 142, 442, 506]      # uneven documents, one of 5 tokens; pad 506..575
+    out = []
+    for d in (64, 128):
+        for ps, permute in ((16, False), (64, False), (64, True), (16, True)):
+            out.append((cu, 576, 4, 8, 2, d, ps, permute))
+    out.append(([0, 1, 2, 70, 200], 256, 2, 4, 1, 64, 64, True))     # one-token documents, MQA
+    out.append(([0, 500], 512, 8, 4, 4, 128, 16, False))               # one document, MHA
+    return out
+
+
+@pytest.mark.parametrize("cu,kv_total,a,h_q,h_kv,d,ps,permute", _packed_tiny_variants())
+def test_allgather_packed_tiny_all_ranks_all_rows(cu, kv_total, a, h_q, h_kv, d, ps, permute):
+    """Every rank's slice of a packed sequence, every row: documents start at
+    unaligned keys, so tiles straddle page boundaries; pad rows are zero."""
+    share = kv_total // a
+    for r in range(a):
+        q, kg, vg, out, scale = _packed_run(cu, r * share, share, h_q, h_kv, d, ps, kv_total, 31 + r, permute)
+        ref = oatt.allgather_kv_packed(q, kg, vg, cu, r * share, scale)
+        gc.assert_close(out, ref, f"packed rank {r} d={d} ps={ps} permute={permute}")
+        pad0 = max(0, cu[-1] - r * share)
+        assert torch.all(out[pad0:] == 0)
+
+
+@pytest.mark.parametrize("rank,h_q,h_kv", [(1, 32, 8), (3, 32, 8), (1, 32, 1), (1, 16, 4), (3, 16, 4)])
+def test_allgather_packed_s32768_sampled(rank, h_q, h_kv):
+    """The packed AllGather-KV workload at full size (7 documents in 30000 real
+    rows of 32768, A = 4): ranks 1 (four documents) and 3 (two documents and
+    the pad suffix), GQA, MQA and the Ulysses U = 2 head share (16/4).  Rows
+    around every document boundary, the slice ends and random rows."""
+    w = W["allgather_packed_s32768"]
+    cu = synth.packed_doc_cu(w)
+    share = w.kv_total // w.ag_degree
+    q0 = rank * share
+    q, kg, vg, out, scale = _packed_run(cu, q0, share, h_q, h_kv, w.d, w.page_size, w.kv_total, w.seed, False)
+    assert torch.isfinite(out).all()
+    rng = np.random.default_rng(rank * 100 + h_kv)
+    rows = {0, 1, share - 1} | set(rng.integers(0, share, 24).tolist())
+    for c in cu:
+        for dr in (-1, 0, 1):
+            if 0 <= c - q0 + dr < share:
+                rows.add(c - q0 + dr)
+    rows = sorted(rows)
+    ref = oatt.allgather_kv_packed(q, kg, vg, cu, q0, scale, rows=rows)
+    print("packed rank", rank, "heads", h_q, h_kv, "err", gc.assert_close(out[rows], ref, "packed s32768"), flush=True)
+    if q0 + share > cu[-1]:
+        assert torch.all(out[cu[-1] - q0:] == 0)
