@@ -129,38 +129,55 @@ def test_allgather_pad_rows_and_ragged(h_kv, q_real, q_total, kv_real):
     assert torch.all(out[q_real:] == 0)
 
 
-def test_prefix_extend_kv_includes_cached_prefix():
+def _prefix_extend_case(cp, lens, prefix, h_q, h_kv, d, ps, seed, sample=None):
     """Cached prefix ahead of the extend part: kv_len grows by the prefix and
-    the causal alignment stays bottom-right."""
-    cp, lens, prefix = 2, [96, 40], [64, 0]
-    h_q, h_kv, d, ps = 8, 2, 128, 16
+    the causal alignment stays bottom-right.  The pool holds prefix and
+    extend keys of every sequence (filled by plain indexing); ``sample`` rows
+    per rank are compared (None: every row)."""
     full = [p + e for p, e in zip(prefix, lens)]
-    qg, kg, vg = synth.normal_bf16(31, (sum(full), h_q, d), (sum(full), h_kv, d), (sum(full), h_kv, d))
+    bs = len(lens)
+    qg, kg, vg = synth.normal_bf16(seed, (sum(full), h_q, d), (sum(full), h_kv, d), (sum(full), h_kv, d))
     starts = np.concatenate([[0], np.cumsum(full)])
-    k_seqs = [kg[starts[b]:starts[b + 1]] for b in range(2)]
-    v_seqs = [vg[starts[b]:starts[b + 1]] for b in range(2)]
-    q_ext = torch.cat([qg[starts[b] + prefix[b]:starts[b + 1]] for b in range(2)])
-    w = synth.Workload(name="pfx", seed=31, causal=True, h_q=h_q, h_kv=h_kv, d=d, page_size=ps,
+    k_seqs = [kg[starts[b]:starts[b + 1]] for b in range(bs)]
+    v_seqs = [vg[starts[b]:starts[b + 1]] for b in range(bs)]
+    q_ext = torch.cat([qg[starts[b] + prefix[b]:starts[b + 1]] for b in range(bs)])
+    w = synth.Workload(name="pfx", seed=seed, causal=True, h_q=h_q, h_kv=h_kv, d=d, page_size=ps,
                        contiguous_kv=False, cp_size=cp)
     indptr, indices, npages = synth.page_table(w, full)
     rows = gc.pool_rows(full, prefix, indptr, indices, ps)
     kp = torch.zeros(npages * ps, h_kv, d, dtype=torch.bfloat16)
     vp = torch.zeros_like(kp)
-    for b in range(2):
+    for b in range(bs):
         kp[torch.from_numpy(rows[b])] = k_seqs[b]
         vp[torch.from_numpy(rows[b])] = v_seqs[b]
+    kp, vp = kp.view(npages, ps, h_kv, d).cuda(), vp.view(npages, ps, h_kv, d).cuda()
     from oracle import layout
     for r in range(cp):
         mo = zigzag_meta.build(cp, r, sum(lens), seq_lens=full, extend_lens=lens)
         q_loc = torch.from_numpy(layout.shard(q_ext.view(torch.int16).numpy(), mo)).view(torch.bfloat16)
         meta = cpa.meta_build(cp, r, lens, seq_lens=full, attn_group=h_q // h_kv, device="cuda")
         out = torch.empty(q_loc.shape, dtype=torch.bfloat16, device="cuda")
-        cpa.prefill_attn(q_loc.cuda(), kp.view(npages, ps, h_kv, d).cuda(), vp.view(npages, ps, h_kv, d).cuda(),
-                         out, meta, 1 / math.sqrt(d), ps, torch.from_numpy(indptr).cuda(),
+        cpa.prefill_attn(q_loc.cuda(), kp, vp, out, meta, 1 / math.sqrt(d), ps, torch.from_numpy(indptr).cuda(),
                          torch.from_numpy(indices).cuda())
         torch.cuda.synchronize()
-        ref = oatt.zigzag_rank(q_loc, k_seqs, v_seqs, mo, 1 / math.sqrt(d))
-        gc.assert_close(out, ref, f"prefix rank {r}")
+        if sample is None:
+            ref = oatt.zigzag_rank(q_loc, k_seqs, v_seqs, mo, 1 / math.sqrt(d))
+            gc.assert_close(out, ref, f"prefix rank {r}")
+        else:
+            loc = gc.sample_rows(mo, meta.q_tile, sample, seed + r)
+            ref = oatt.zigzag_rank_rows(q_loc, loc, k_seqs, v_seqs, mo, 1 / math.sqrt(d))
+            print("prefix rank", r, "err", gc.assert_close(out[loc], ref, f"prefix rank {r}"), flush=True)
+
+
+def test_prefix_extend_kv_includes_cached_prefix():
+    _prefix_extend_case(2, [96, 40], [64, 0], 8, 2, 128, 16, 31)
+
+
+def test_prefix_extend_p4096_e8192_cp4_sampled():
+    """Prefix-cached extend at size: a 4096-token cached prefix ahead of an
+    8192-token extend, next to a sequence without prefix (6144 tokens), cp = 4,
+    GQA 32/4, pages of 64 with permuted ids; sampled rows of every rank."""
+    _prefix_extend_case(4, [8192, 6144], [4096, 0], 32, 4, 128, 64, 41, sample=24)
 
 
 def test_mha_and_mqa_group_shapes():
