@@ -504,12 +504,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       wait_tile(t + 1);
       step_barrier();
     };
-    // The last tile's PV products and its block-1 softmax (stage st).
-    auto finish = [&](auto stc) {
-      pv_blk(stc, I0{}, pk);
-      sm_blk(s1, pk + 8);
-      pv_blk(stc, I1{}, pk + 8);
-    };
 
     int t = 1;
     const int t_full_end = max(1, t_mask);          // tiles [1, t_mask) need no mask
