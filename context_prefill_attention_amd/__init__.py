@@ -48,7 +48,8 @@ class CMeta(ctypes.Structure):
         ("total_q_prev_tokens", _i32), ("total_q_next_tokens", _i32),
         ("max_seqlen_q_prev", _i32), ("max_seqlen_q_next", _i32), ("n_local_rows", _i32),
         ("n_chunks", _i32), ("max_chunk_rows", _i32), ("n_seg", _i32), ("n_work", _i32),
-        ("max_kv_len", _i32), ("q_tile", _i32), ("blob_bytes", _i64),
+        ("max_kv_len", _i32), ("q_tile", _i32), ("kv_align", _i32), ("reserved", _i32),
+        ("blob_bytes", _i64),
         ("off_split_list", _i64), ("off_zigzag_index", _i64), ("off_cp_reverse_index", _i64),
         ("off_reverse_split_len", _i64), ("off_per_rank_actual_token", _i64),
         ("off_kv_len_prev", _i64), ("off_kv_len_next", _i64), ("off_q_prev", _i64),

@@ -127,9 +127,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
-// PAGE_PER_TILE: pages hold >= 64 keys, so a tile lies in one page and its id
-// is one scalar load; otherwise every lane looks up its own row's page.
-template <int D, bool PAGE_PER_TILE>
+// Page modes.  PM == kPageTile: pages hold >= 64 keys, a tile lies in one
+// page (or, after an unaligned segment start, two) and its id is one scalar
+// load.  PM in {16, 32}: pages of PM keys and every segment starts on a
+// page boundary, so a tile holds 64/PM whole pages whose ids are again
+// scalar loads.  PM == kPageLane (pages under 16 keys, or unaligned
+// segments): every lane looks up its own row's page with a vector load.
+constexpr int kPageLane = 0, kPageTile = 1;
+
+template <int D, int PM>
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   constexpr int NC = D / 8;               // 16-byte chunks per K/V row
   constexpr int KSTEPS = D / 16;          // k-steps of S^T = K Q^T
@@ -137,7 +143,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   constexpr int ROW_BYTES = D * 2;
   constexpr int TILE_BYTES = kAttnKeys * ROW_BYTES;    // one K (or V) tile
   constexpr int LOADS = TILE_BYTES / (kThreads * 16);  // 16-byte direct loads per lane per K (or V) tile
-  constexpr int PLOADS = PAGE_PER_TILE ? 0 : LOADS;    // vector page-id loads per lane per tile
+  constexpr bool PAGE_PER_TILE = PM == kPageTile;
+  constexpr int GP = PM >= 16 ? PM : 0;                // page size of the group modes
+  constexpr int NPP = GP ? kAttnKeys / GP : 1;         // pages per tile in the group modes
+  constexpr int PLOADS = PM == kPageLane ? LOADS : 0;  // vector page-id loads per lane per tile
   static_assert(LOADS >= 1 && TILE_BYTES % (kThreads * 16) == 0, "loader shape");
   // K and V rings of kStages tiles, one array per stage: the compiler can
   // then tell the stage being read from the stages whose direct loads are
@@ -230,13 +239,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   // leave the younger tiles in flight.
   // With pages of >= 64 keys: the page of the tile's first key and, if the
   // tile may straddle a page boundary, the next one.
-  struct Pages { int p[PAGE_PER_TILE ? 2 : LOADS]; };
+  // Group modes: the tile's NPP pages as scalars (pg.p[j] = page of keys
+  // j*GP .. j*GP+GP-1 of the tile); lane lookups: the page of each of this
+  // lane's rows.
+  constexpr int NPG = PAGE_PER_TILE ? 2 : (GP != 0 ? NPP : LOADS);
+  struct Pages { int p[NPG]; };
   auto fetch_pages = [&](int t) -> Pages {
     Pages pg;
     if constexpr (PAGE_PER_TILE) {
       const int e0 = (kv0 + min(t, n_tiles - 1) * kAttnKeys) >> shift;
       pg.p[0] = ptab[e0];
       pg.p[1] = straddle ? ptab[min(e0 + 1, n_entries - 1)] : pg.p[0];
+    } else if constexpr (GP != 0) {
+      const int e0 = (kv0 + min(t, n_tiles - 1) * kAttnKeys) >> shift;
+#pragma unroll
+      for (int j = 0; j < NPP; ++j) pg.p[j] = ptab[min(e0 + j, n_entries - 1)];
     } else {
 #pragma unroll
       for (int u = 0; u < LOADS; ++u) {
@@ -277,8 +294,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       const int key = t * kAttnKeys + ld_row[u];
       const int pos = kv0 + key;
       int page;
-      if constexpr (PAGE_PER_TILE) page = (pos >> shift) == (first >> shift) ? pg.p[0] : pg.p[1];
-      else page = pg.p[u];
+      if constexpr (PAGE_PER_TILE) {
+        page = (pos >> shift) == (first >> shift) ? pg.p[0] : pg.p[1];
+      } else if constexpr (GP != 0) {
+        // Page j = ld_row[u] / GP of the tile holds this lane's row, chosen
+        // by a tree of selects on the bits of j (a flat compare chain would
+        // be turned into an indexed array in memory).
+        const int j = ld_row[u] / GP;
+        static_assert(NPP == 2 || NPP == 4, "group modes hold 2 or 4 pages per tile");
+        const int q0 = pg.p[0] ^ ((pg.p[0] ^ pg.p[1]) & -(j & 1));
+        if constexpr (NPP == 2) {
+          page = q0;
+        } else {
+          const int q1 = (j & 1) ? pg.p[3] : pg.p[2];
+          page = (j & 2) ? q1 : q0;
+        }
+      } else {
+        page = pg.p[u];
+      }
       const bool ok = key < s.kv_len && page >= 0 && page < a.num_pages;
       const int64_t tok = ok ? ((int64_t)page << shift | (pos & ps_mask))
                              : (page0_ok ? (int64_t)page0 << shift : 0);
@@ -293,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   // issued after them: the page ids of tile t+2 (with small pages) and the
   // loads of tile t+1, if those tiles exist.
   auto wait_tile = [&](int t) {
-    if (t + 2 < n_pad) wait_vmcnt<PLOADS + 2 * LOADS>();
+    if (PLOADS != 0 && t + 2 < n_pad) wait_vmcnt<PLOADS + 2 * LOADS>();
     else if (t + 1 < n_pad) wait_vmcnt<2 * LOADS>();
     else wait_vmcnt<0>();
   };
@@ -602,15 +635,28 @@ extern "C" int cp_prefill_attn(const void* q, const void* k_pool, const void* v_
   while ((1 << shift) < page_size) ++shift;
   args.page_shift = shift;
   args.scale_log2 = scale * 1.4426950408889634f;
-  const bool page_per_tile = shift >= 6;   // pages of >= 64 keys: one page per key tile
-  if (D == 128 && page_per_tile)
-    hipLaunchKernelGGL((attn_kernel<128, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
-  else if (D == 128)
-    hipLaunchKernelGGL((attn_kernel<128, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
-  else if (page_per_tile)
-    hipLaunchKernelGGL((attn_kernel<64, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
-  else
-    hipLaunchKernelGGL((attn_kernel<64, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
+  // Page mode: one page per tile (>= 64 keys), whole pages per tile (16 or
+  // 32 keys, segments starting on page boundaries), or a lookup per lane.
+  const int pm = shift >= 6 ? kPageTile
+                 : (shift >= 4 && meta->kv_align >= page_size ? (1 << shift) : kPageLane);
+  const dim3 g((unsigned)grid), b(kThreads);
+#define CP_LAUNCH(DD, PMV) hipLaunchKernelGGL((attn_kernel<DD, PMV>), g, b, 0, stream, args)
+  if (D == 128) {
+    switch (pm) {
+      case kPageTile: CP_LAUNCH(128, kPageTile); break;
+      case 32: CP_LAUNCH(128, 32); break;
+      case 16: CP_LAUNCH(128, 16); break;
+      default: CP_LAUNCH(128, kPageLane); break;
+    }
+  } else {
+    switch (pm) {
+      case kPageTile: CP_LAUNCH(64, kPageTile); break;
+      case 32: CP_LAUNCH(64, 32); break;
+      case 16: CP_LAUNCH(64, 16); break;
+      default: CP_LAUNCH(64, kPageLane); break;
+    }
+  }
+#undef CP_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(CP_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   return CP_OK;

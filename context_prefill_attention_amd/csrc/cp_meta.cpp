@@ -89,6 +89,8 @@ int check_group(int32_t g, bool allow_zero) {
   return CP_OK;
 }
 
+constexpr int32_t kKvAlignMax = 1 << 30;   // kv_align when every segment starts at key 0
+
 void write_i32(void* blob, int64_t off, const std::vector<int32_t>& v) {
   if (!v.empty()) std::memcpy(static_cast<char*>(blob) + off, v.data(), v.size() * 4);
 }
@@ -278,6 +280,7 @@ extern "C" int cp_meta_build(int32_t cp_size, int32_t cp_rank, int32_t bs,
   m.n_work = (int32_t)work.size();
   m.max_kv_len = max_kv;
   m.q_tile = q_tile;
+  m.kv_align = kKvAlignMax;
   m.off_split_list = lay.take(4LL * bs * nblk);
   m.off_zigzag_index = lay.take(4LL * 2 * bs);
   m.off_cp_reverse_index = lay.take(4LL * bs * nblk);
@@ -353,6 +356,7 @@ extern "C" int cp_allgather_meta_build(int32_t q_total, int32_t q_real, int32_t 
   m.n_work = (int32_t)work.size();
   m.max_kv_len = kv_len;
   m.q_tile = q_tile;
+  m.kv_align = kKvAlignMax;
   const int64_t empty = lay.take(0);
   m.off_split_list = m.off_zigzag_index = m.off_cp_reverse_index = m.off_reverse_split_len = empty;
   m.off_per_rank_actual_token = m.off_kv_len_prev = m.off_kv_len_next = empty;
@@ -424,12 +428,16 @@ extern "C" int cp_allgather_packed_meta_build(int32_t n_docs, const int32_t* doc
   m.version = CP_META_VERSION;
   m.kind = CP_META_ALLGATHER;
   m.bs = 1;   // one page-table row: the ordered global K/V
+  int32_t align = kKvAlignMax;
+  for (const Seg& g : segs)
+    if (g.kv_start != 0) align = std::min(align, g.kv_start & -g.kv_start);
   m.attn_group = attn_group;
   m.n_local_rows = q_total;
   m.n_seg = (int32_t)segs.size();
   m.n_work = (int32_t)work.size();
   m.max_kv_len = max_kv;
   m.q_tile = q_tile;
+  m.kv_align = align;
   const int64_t empty = lay.take(0);
   m.off_split_list = m.off_zigzag_index = m.off_cp_reverse_index = m.off_reverse_split_len = empty;
   m.off_per_rank_actual_token = m.off_kv_len_prev = m.off_kv_len_next = empty;

@@ -54,7 +54,7 @@ typedef enum cp_status {
   CP_ERR_HIP = -5               /* the HIP runtime reported an error at launch */
 } cp_status_t;
 
-enum { CP_META_VERSION = 1 };
+enum { CP_META_VERSION = 2 };
 enum { CP_META_ZIGZAG = 1, CP_META_ALLGATHER = 2 };
 enum { CP_RERANGE_GATHERED_TO_ORIG = 0, CP_RERANGE_ORIG_TO_GATHERED = 1 };
 
@@ -98,6 +98,9 @@ typedef struct cp_meta {
   int32_t n_work;             /* attention work items */
   int32_t max_kv_len;
   int32_t q_tile;             /* query positions per work item */
+  int32_t kv_align;           /* largest power of two (<= 2^30) dividing every segment's first key
+                                 position in its page-table row (2^30 when all start at 0) */
+  int32_t reserved;
   int64_t blob_bytes;         /* bytes of the blob that are in use */
   int64_t off_split_list, off_zigzag_index, off_cp_reverse_index, off_reverse_split_len;
   int64_t off_per_rank_actual_token, off_kv_len_prev, off_kv_len_next;
@@ -233,6 +236,10 @@ int cp_kv_scatter(const void* d_blob, const cp_meta_t* meta,
  *     [0, num_pages) is read from the first slot of the segment's page-table
  *     row instead: no out-of-bounds read, but such a table gives unspecified
  *     results.
+ *   meta->kv_align picks how page ids are fetched for pages under 64 keys
+ *     (whole pages per key tile when it is >= page_size); a meta whose
+ *     kv_align overstates the segments' alignment gives unspecified results,
+ *     again with no out-of-bounds read.  The meta builders set it exactly.
  * Requires H_q % H_kv == 0 (else CP_ERR_INVALID_ARG, [P4]), H_q/H_kv equal to
  * meta->attn_group, D in {64, 128}, page_size a power of two, scale finite
  * and > 0.

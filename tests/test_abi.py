@@ -106,8 +106,10 @@ def test_segments_and_work_list(group):
         segs = _unpack(m.blob, m.off_segs, m.n_seg, 8)
         osegs = list(zigzag_meta.segments(o))
         assert len(segs) == len(osegs)
-        for (q_row0, q_len, q_rows, kv_len, off, page_row, causal, _), (_h, b, r0, ql, kl) in zip(segs, osegs):
-            assert (q_row0, q_len, q_rows, kv_len, off, page_row, causal) == (r0, ql, ql, kl, kl - ql, b, 1)
+        for (q_row0, q_len, q_rows, kv_len, off, page_row, causal, kv_start), (_h, b, r0, ql, kl) in zip(segs, osegs):
+            assert (q_row0, q_len, q_rows, kv_len, off, page_row, causal, kv_start) == \
+                (r0, ql, ql, kl, kl - ql, b, 1, 0)
+        assert m.kv_align == 2**30              # every sequence's keys start its page-table row
         work = _unpack(m.blob, m.off_work, m.n_work, 4)
         tq = ROWS_PER_ITEM // group
         assert m.q_tile == tq
@@ -132,6 +134,7 @@ def test_segments_and_work_list(group):
 def test_allgather_meta():
     m = cpa.allgather_meta_build(8192, 8192, 30000, 4)
     assert m.kind == cpa.META_ALLGATHER and m.n_seg == 1 and m.n_local_rows == 8192
+    assert m.kv_align == 2**30
     seg = _unpack(m.blob, m.off_segs, 1, 8)[0]
     assert tuple(seg[:7]) == (0, 8192, 8192, 30000, 0, 0, 0)
     work = _unpack(m.blob, m.off_work, m.n_work, 4)
@@ -175,6 +178,13 @@ def test_allgather_packed_meta(cu, q_start, q_total, group):
     assert m.kind == cpa.META_ALLGATHER and m.n_local_rows == q_total
     segs = _unpack(m.blob, m.off_segs, m.n_seg, 8).tolist()
     assert segs == _expected_packed_segments(cu, q_start, q_total)
+    # kv_align: largest power of two (capped at 2^30) dividing every
+    # segment's first key position in the page-table row
+    starts = [sg[7] for sg in segs if sg[7] != 0]
+    align = 2**30
+    while any(st % align for st in starts):
+        align //= 2
+    assert m.kv_align == align
     work = _unpack(m.blob, m.off_work, m.n_work, 4)
     tq = ROWS_PER_ITEM // group
     assert m.q_tile == tq

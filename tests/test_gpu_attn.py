@@ -223,13 +223,20 @@ def _packed_tiny_variants():
             out.append((cu, 576, 4, 8, 2, d, ps, permute))
     out.append(([0, 1, 2, 70, 200], 256, 2, 4, 1, 64, 64, True))     # one-token documents, MQA
     out.append(([0, 500], 512, 8, 4, 4, 128, 16, False))               # one document, MHA
+    # documents starting on page boundaries (a tile's pages are whole pages of
+    # one document's row range), and one aligned only to half a page
+    out.append(([0, 64, 96, 352, 480], 576, 4, 8, 2, 128, 32, True))
+    out.append(([0, 48, 64, 208, 400, 464], 576, 4, 8, 2, 128, 16, True))
+    out.append(([0, 8, 136, 200, 504], 576, 4, 8, 1, 64, 8, True))
+    out.append(([0, 48, 208, 512], 576, 4, 8, 2, 128, 32, True))
     return out
 
 
 @pytest.mark.parametrize("cu,kv_total,a,h_q,h_kv,d,ps,permute", _packed_tiny_variants())
 def test_allgather_packed_tiny_all_ranks_all_rows(cu, kv_total, a, h_q, h_kv, d, ps, permute):
-    """Every rank's slice of a packed sequence, every row: documents start at
-    unaligned keys, so tiles straddle page boundaries; pad rows are zero."""
+    """Every rank's slice of a packed sequence, every row: documents starting
+    at unaligned keys (tiles straddle page boundaries) or on page boundaries
+    of 8, 16 or 32 keys; pad rows are zero."""
     share = kv_total // a
     for r in range(a):
         q, kg, vg, out, scale = _packed_run(cu, r * share, share, h_q, h_kv, d, ps, kv_total, 31 + r, permute)
