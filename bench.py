@@ -11,6 +11,12 @@ Default workload: cp_size=8, one sequence of 131072 tokens (blocks of 8192),
 rank 3 (blocks 3 and 12; kv_len 32768 and 106496), H_q=64, H_kv=8, D=128,
 paged KV with page size 64 and permuted pages, bf16.
 
+``--workload`` picks any other synthetic workload.  For the AllGather-KV
+shares (local Q against the ordered global K/V, whose pad suffix is never
+read) a step is the host metadata, its copy and the non-causal attention
+launch; ``--rank`` picks the rank's slice, ``--kv-heads`` the KV head
+count and ``--q-heads`` the query head count (the Ulysses head share).
+
 Prints one JSON line.  ``value`` is useful attention TFLOP/s over the whole
 step (masked-out pairs and skipped tiles are not counted).
 """
@@ -46,7 +52,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_cp8_s131072_r3")
-    ap.add_argument("--rank", type=int, default=None, help="CP rank (zigzag workloads)")
+    ap.add_argument("--rank", type=int, default=None, help="CP rank (zigzag) or AllGather-KV rank")
+    ap.add_argument("--kv-heads", type=int, default=None, help="KV heads (AllGather-KV workloads)")
+    ap.add_argument("--q-heads", type=int, default=None,
+                    help="query heads (AllGather-KV workloads; e.g. the share a Ulysses group leaves on one GPU)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=768, help="query rows in the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -67,18 +76,27 @@ def calibrate_copy(steps: int) -> None:
                       dst.numel() * 2, "launches": steps}))
 
 
-def traffic_for(kernel_src: str):
+def traffic_for(kernel_src: str, workload: str, rank: int):
     """Measured HBM bytes per attention launch, if the committed counter
-    summary was taken on this exact kernel source."""
+    summary was taken on this exact kernel source, workload and rank."""
     path = os.path.join(ROOT, "profiles", "attn_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
-    if rec.get("kernel_sha256") != sha:
+    if rec.get("kernel_sha256") != sha or rec.get("workload") != workload or rec.get("rank") != rank:
         return None
     return rec.get("bytes_per_launch")
+
+
+def oracle_threads() -> int:
+    """BLAS threads the oracle's numpy runs on."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count() or 1
 
 
 def cpu_baseline(w, meta_lists, q_loc, k_seq, v_seq, n_rows: int):
@@ -86,11 +104,7 @@ def cpu_baseline(w, meta_lists, q_loc, k_seq, v_seq, n_rows: int):
     same rank share; scale to useful TFLOP/s."""
     import numpy as np
     from oracle import attention as oatt
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = oracle_threads()
     segs = meta_lists["segments"]
     per = max(1, n_rows // len(segs))
     scale = 1.0 / math.sqrt(w.d)
@@ -110,26 +124,86 @@ def cpu_baseline(w, meta_lists, q_loc, k_seq, v_seq, n_rows: int):
                       f"of the same rank share, all visible keys, numpy float64; {dt:.1f} s"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: the exchange between GPUs is not implemented (asked for --gpus {args.gpus}).",
-              file=sys.stderr)
-        sys.exit(2)
-    if args.calibrate_copy:
-        calibrate_copy(args.steps)
-        return
-    import torch
-    import context_prefill_attention_amd as cpa
-    import synth
+def cpu_baseline_allgather(w, h_q, q_loc, k_g, v_g, doc_cu, q_start, n_rows: int, packed: bool):
+    """Time the fp64 oracle on evenly spaced local query rows of the
+    AllGather-KV share; scale to useful TFLOP/s."""
+    import numpy as np
+    from oracle import attention as oatt
+    threads = oracle_threads()
+    n = q_loc.shape[0]
+    rows = sorted(set(np.linspace(0, n - 1, n_rows).astype(np.int64).tolist()))
+    scale = 1.0 / math.sqrt(w.d)
+    t0 = time.perf_counter()
+    if packed:
+        oatt.allgather_kv_packed(q_loc, k_g, v_g, doc_cu, q_start, scale, rows=rows)
+    else:
+        q_real = max(0, min(n, doc_cu[-1] - q_start))
+        oatt.allgather_kv(q_loc, k_g, v_g, q_real, doc_cu[-1], scale, rows=rows)
+    dt = time.perf_counter() - t0
+    visible = 0
+    for r in rows:
+        g = q_start + r
+        for b in range(len(doc_cu) - 1):
+            if doc_cu[b] <= g < doc_cu[b + 1]:
+                visible += doc_cu[b + 1] - doc_cu[b]
+    flops = 4 * w.d * h_q * visible
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(rows)} evenly spaced local query rows x {h_q} heads of the same share, "
+                      f"all visible keys, numpy float64; {dt:.1f} s"}
 
-    w = synth.WORKLOADS[args.workload]
-    if not w.causal:
-        print("bench.py times the zigzag (causal) workloads", file=sys.stderr)
-        sys.exit(2)
+
+def run_timed(torch, step, names, warmup: int, steps: int):
+    """Run ``warmup`` untimed steps, then ``steps`` timed ones.  step(ev)
+    records ev[i] before phase names[i] and ev[-1] after the last phase (ev
+    is None when untimed).  Returns (wall ms per step, {phase: mean ms})."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    acc = dict.fromkeys(names, 0.0)
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(ev)
+        torch.cuda.synchronize()   # per step, so the events of every step can be read
+        for i, n in enumerate(names):
+            acc[n] += ev[i].elapsed_time(ev[i + 1])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, {n: v / steps for n, v in acc.items()}
+
+
+def result_line(args, useful_flops: float, ms_step: float, attn_ms: float, config: dict,
+                traffic) -> dict:
+    attn_tflops = useful_flops / (attn_ms * 1e-3) / 1e12
+    return {
+        "metric": "CP-rank prefill attn useful TFLOP/s (% MI355X bf16 MFMA peak); rerange GB/s",
+        "value": round(useful_flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": config,
+        "attn_ms": round(attn_ms, 4),
+        "attn_useful_tflops": round(attn_tflops, 2),
+        "attn_frac_of_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+
+
+KERNEL_SRC = os.path.join(ROOT, "context_prefill_attention_amd", "csrc", "cp_attn.hip")
+
+
+def run_zigzag(args, w, torch, cpa, synth) -> dict:
     rank = w.ranks[0] if args.rank is None else args.rank
     dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
     lens = synth.sequence_lengths(w)
     total = sum(lens)
     group = w.h_q // w.h_kv
@@ -156,79 +230,130 @@ def main():
     rerange_bytes = 2 * 2 * total * row_bytes      # K and V, each read once and written once
     scatter_bytes = 2 * 2 * total * row_bytes
 
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    stats = {"scatter": 0.0, "rerange": 0.0, "attn": 0.0}
-
-    def step(record: bool):
+    def step(ev):
         meta = cpa.meta_build(w.cp_size, rank, lens, attn_group=group, device=dev)
-        if record:
+        if ev:
             ev[0].record()
         cpa.kv_scatter(meta, k_gd, v_gd, k_pool, v_pool, w.page_size, ip, ix)
-        if record:
+        if ev:
             ev[1].record()
         cpa.zigzag_rerange(meta, k_gd, k_orig, cpa.GATHERED_TO_ORIG)
         cpa.zigzag_rerange(meta, v_gd, v_orig, cpa.GATHERED_TO_ORIG)
-        if record:
+        if ev:
             ev[2].record()
         cpa.prefill_attn(q_d, k_pool, v_pool, out, meta, scale, w.page_size, ip, ix)
-        if record:
+        if ev:
             ev[3].record()
-        return meta
 
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-        torch.cuda.synchronize()   # per step, so the events of every step can be read
-        stats["scatter"] += ev[0].elapsed_time(ev[1])
-        stats["rerange"] += ev[1].elapsed_time(ev[2])
-        stats["attn"] += ev[2].elapsed_time(ev[3])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    attn_ms = stats["attn"] / args.steps
-    rer_ms = stats["rerange"] / args.steps
-    sc_ms = stats["scatter"] / args.steps
+    ms_step, ph = run_timed(torch, step, ["scatter", "rerange", "attn"], args.warmup, args.steps)
     if not torch.isfinite(out).all():
         print("non-finite attention output", file=sys.stderr)
         sys.exit(1)
-
-    attn_tflops = useful_flops / (attn_ms * 1e-3) / 1e12
-    kernel_src = os.path.join(ROOT, "context_prefill_attention_amd", "csrc", "cp_attn.hip")
-    res = {
-        "metric": "CP-rank prefill attn useful TFLOP/s (% MI355X bf16 MFMA peak); rerange GB/s",
-        "value": round(useful_flops / (ms_step * 1e-3) / 1e12, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": w.name, "cp_size": w.cp_size, "cp_rank": rank, "bs": len(lens),
-                   "seq_len": total, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.d,
-                   "page_size": w.page_size, "parallelism": "one CP rank's share on one GPU"},
-        "attn_ms": round(attn_ms, 4),
-        "attn_useful_tflops": round(attn_tflops, 2),
-        "attn_frac_of_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-        "rerange_kv_ms": round(rer_ms, 4),
-        "rerange_gbps": round(rerange_bytes / (rer_ms * 1e-3) / 1e9, 1),
-        "scatter_kv_ms": round(sc_ms, 4),
-        "scatter_gbps": round(scatter_bytes / (sc_ms * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_for(kernel_src)},
-    }
+    config = {"workload": w.name, "cp_size": w.cp_size, "cp_rank": rank, "bs": len(lens),
+              "seq_len": total, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.d,
+              "page_size": w.page_size, "parallelism": "one CP rank's share on one GPU"}
+    res = result_line(args, useful_flops, ms_step, ph["attn"], config,
+                      traffic_for(KERNEL_SRC, w.name, rank))
+    roofline = res.pop("roofline")
+    res.update({
+        "rerange_kv_ms": round(ph["rerange"], 4),
+        "rerange_gbps": round(rerange_bytes / (ph["rerange"] * 1e-3) / 1e9, 1),
+        "scatter_kv_ms": round(ph["scatter"], 4),
+        "scatter_gbps": round(scatter_bytes / (ph["scatter"] * 1e-3) / 1e9, 1),
+        "roofline": roofline,
+    })
     if not args.no_cpu_baseline:
         # the oracle reads synthetic token-order K/V of the same shape (its
         # timing does not depend on the values)
         res["cpu_baseline"] = cpu_baseline(w, {"segments": segs}, q_loc, k_g[:total], v_g[:total],
                                            args.cpu_rows)
+    return res
+
+
+def run_allgather(args, w, torch, cpa, synth) -> dict:
+    rank = w.ag_rank if args.rank is None else args.rank
+    h_kv = w.h_kv if args.kv_heads is None else args.kv_heads
+    h_q = w.h_q if args.q_heads is None else args.q_heads
+    if not 0 <= rank < w.ag_degree or h_kv < 1 or h_q < 1 or h_q % h_kv != 0:
+        print(f"bad --rank {rank} (0..{w.ag_degree - 1}), --q-heads {h_q} or --kv-heads {h_kv} "
+              f"(a divisor of the query heads)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda", 0)
+    packed = w.packed_docs is not None
+    share = w.kv_total // w.ag_degree
+    q_start = rank * share
+    doc_cu = synth.packed_doc_cu(w) if packed else [0, w.kv_real]
+    q_real = max(0, min(share, w.kv_real - q_start))
+    group = h_q // h_kv
+
+    def build(device):
+        if packed:
+            return cpa.allgather_packed_meta_build(doc_cu, q_start, share, group, device=device)
+        return cpa.allgather_meta_build(share, q_real, w.kv_real, group, device=device)
+
+    qg, k_g, v_g = synth.normal_bf16(w.seed, (w.kv_total, h_q, w.d), (w.kv_total, h_kv, w.d),
+                                     (w.kv_total, h_kv, w.d))
+    k_g[w.kv_real:] = float("nan")     # the pad suffix must never be read
+    v_g[w.kv_real:] = float("nan")
+    q_loc = qg[q_start:q_start + share].contiguous()
+    n_pages = w.kv_total // w.page_size
+    q_d = q_loc.to(dev)
+    k_pool = k_g.to(dev).view(n_pages, w.page_size, h_kv, w.d)   # contiguous K/V: identity table
+    v_pool = v_g.to(dev).view(n_pages, w.page_size, h_kv, w.d)
+    ip = torch.tensor([0, n_pages], dtype=torch.int32, device=dev)
+    ix = torch.arange(n_pages, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q_d)
+    scale = 1.0 / math.sqrt(w.d)
+    pairs = sum(max(0, min(doc_cu[b + 1], q_start + share) - max(doc_cu[b], q_start)) *
+                (doc_cu[b + 1] - doc_cu[b]) for b in range(len(doc_cu) - 1))
+    useful_flops = 4 * w.d * h_q * pairs
+
+    def step(ev):
+        meta = build(dev)
+        if ev:
+            ev[0].record()
+        cpa.prefill_attn(q_d, k_pool, v_pool, out, meta, scale, w.page_size, ip, ix)
+        if ev:
+            ev[1].record()
+
+    ms_step, ph = run_timed(torch, step, ["attn"], args.warmup, args.steps)
+    if not torch.isfinite(out).all():
+        print("non-finite attention output", file=sys.stderr)
+        sys.exit(1)
+    config = {"workload": w.name, "ag_degree": w.ag_degree, "ag_rank": rank, "q_rows": share,
+              "kv_total": w.kv_total, "kv_real": w.kv_real, "n_docs": len(doc_cu) - 1,
+              "h_q": h_q, "h_kv": h_kv, "head_dim": w.d, "page_size": w.page_size,
+              "parallelism": "one AllGather-KV rank's share on one GPU"}
+    res = result_line(args, useful_flops, ms_step, ph["attn"], config,
+                      traffic_for(KERNEL_SRC, w.name, rank))
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_allgather(w, h_q, q_loc, k_g, v_g, doc_cu, q_start,
+                                                     args.cpu_rows, packed)
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the exchange between GPUs is not implemented (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.steps)
+        return
+    import torch
+    import context_prefill_attention_amd as cpa
+    import synth
+
+    if args.workload not in synth.WORKLOADS:
+        print(f"unknown workload {args.workload}; one of {sorted(synth.WORKLOADS)}", file=sys.stderr)
+        sys.exit(2)
+    w = synth.WORKLOADS[args.workload]
+    if w.causal and (args.kv_heads is not None or args.q_heads is not None):
+        print("--kv-heads and --q-heads apply to the AllGather-KV workloads", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    res = run_zigzag(args, w, torch, cpa, synth) if w.causal else run_allgather(args, w, torch, cpa, synth)
     print(json.dumps(res), flush=True)
 
 
