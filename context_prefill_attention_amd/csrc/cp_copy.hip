@@ -76,10 +76,13 @@ __global__ __launch_bounds__(kCopyThreads) void rerange_narrow_kernel(
   for (int64_t i = threadIdx.x; i < n; i += kCopyThreads) d[i] = s[i];
 }
 
-constexpr int kScatterRows = 16;  // token rows per workgroup
+constexpr int kScatterRows = 16;   // token rows per workgroup
+constexpr int kScatterUnroll = 4;  // 16-B vectors of K and of V per lane in flight
 
 // One workgroup copies rows [part*16, part*16+16) of chunk c, for K and V.
-// The destination row of every token is looked up once, into LDS.
+// The destination row of every token is looked up once, into LDS.  Vector i
+// of the block (i = lane + k*threads) is row i / vpr, column i % vpr; each
+// lane steps its (row, column) pair by the thread count without dividing.
 __global__ __launch_bounds__(kCopyThreads) void scatter_kernel(
     const Chunk* __restrict__ chunks, int32_t parts_per_chunk,
     const unsigned char* __restrict__ kg, const unsigned char* __restrict__ vg,
@@ -100,28 +103,35 @@ __global__ __launch_bounds__(kCopyThreads) void scatter_kernel(
     dst_row[threadIdx.x] = (page >= 0 && page < num_pages) ? (int64_t)page * page_size + pos % page_size : -1;
   }
   __syncthreads();
-  const int64_t vec_per_row = row_bytes / 16;
-  const int64_t total = vec_per_row * nrows;
-  const int64_t src_row0 = (int64_t)ch.g_row + r0;
-  for (int64_t i0 = 0; i0 < total; i0 += (int64_t)kCopyThreads * 2) {
-    u32x4 a[2], b[2];
-    int64_t rr[2], cc[2];
-    bool ok[2];
+  const int vpr = (int)(row_bytes / 16);   // the host keeps kScatterRows * vpr within int32
+  const int total = vpr * nrows;
+  const int dr = kCopyThreads / vpr, dc = kCopyThreads - dr * vpr;
+  int r = (int)threadIdx.x / vpr;
+  int col = (int)threadIdx.x - r * vpr;
+  const unsigned char* ks = kg + ((int64_t)ch.g_row + r0) * row_bytes;
+  const unsigned char* vs = vg + ((int64_t)ch.g_row + r0) * row_bytes;
+  for (int i0 = 0; i0 < total; i0 += kCopyThreads * kScatterUnroll) {
+    u32x4 a[kScatterUnroll], b[kScatterUnroll];
+    int rr[kScatterUnroll], cc[kScatterUnroll];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int64_t i = i0 + u * kCopyThreads + threadIdx.x;
-      ok[u] = i < total;
-      rr[u] = ok[u] ? i / vec_per_row : 0;
-      cc[u] = ok[u] ? i - rr[u] * vec_per_row : 0;
-      if (ok[u]) {
-        const int64_t so = (src_row0 + rr[u]) * row_bytes + cc[u] * 16;
-        a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kg + so));
-        b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + so));
+    for (int u = 0; u < kScatterUnroll; ++u) {
+      rr[u] = r;
+      cc[u] = col;
+      if (i0 + u * kCopyThreads + (int)threadIdx.x < total) {
+        const int64_t so = (int64_t)r * row_bytes + col * 16;
+        a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ks + so));
+        b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs + so));
+      }
+      r += dr;
+      col += dc;
+      if (col >= vpr) {
+        col -= vpr;
+        ++r;
       }
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (ok[u] && dst_row[rr[u]] >= 0) {
+    for (int u = 0; u < kScatterUnroll; ++u) {
+      if (i0 + u * kCopyThreads + (int)threadIdx.x < total && dst_row[rr[u]] >= 0) {
         const int64_t dof = dst_row[rr[u]] * row_bytes + cc[u] * 16;
         __builtin_nontemporal_store(a[u], reinterpret_cast<u32x4*>(kp + dof));
         __builtin_nontemporal_store(b[u], reinterpret_cast<u32x4*>(vp + dof));
@@ -189,6 +199,8 @@ extern "C" int cp_kv_scatter(const void* d_blob, const cp_meta_t* meta,
   const int64_t row_bytes = (int64_t)H_kv * D * 2;
   if (row_bytes % 16 != 0)
     return set_error(CP_ERR_UNSUPPORTED, "H_kv*D*2=%lld must be a multiple of 16", (long long)row_bytes);
+  if (row_bytes / 16 * kScatterRows > 2147483647LL)
+    return set_error(CP_ERR_OVERFLOW, "H_kv*D*2=%lld is too large a row", (long long)row_bytes);
   if (page_size < 1) return set_error(CP_ERR_INVALID_ARG, "page_size=%d", page_size);
   if (num_pages < 1) return set_error(CP_ERR_INVALID_ARG, "num_pages=%d", num_pages);
   if (!k_gathered || !v_gathered || !k_pool || !v_pool || !kv_page_indptr || !kv_page_indices)
