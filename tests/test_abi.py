@@ -301,6 +301,9 @@ def test_copy_validation_fails_closed(lib):
     assert sc(FAKE, ctypes.byref(m.c), FAKE, FAKE, FAKE, FAKE, 8, 0, 4, 128, FAKE, FAKE, None) == cpa.CP_ERR_INVALID_ARG
     assert sc(FAKE, ctypes.byref(m.c), FAKE, None, FAKE, FAKE, 8, 16, 4, 128, FAKE, FAKE, None) == cpa.CP_ERR_INVALID_ARG
     assert sc(FAKE, ctypes.byref(ag.c), FAKE, FAKE, FAKE, FAKE, 8, 16, 4, 128, FAKE, FAKE, None) == cpa.CP_ERR_INVALID_ARG
+    # 2^31-byte rows: 16 rows of 16-byte vectors per workgroup would pass int32
+    assert sc(FAKE, ctypes.byref(m.c), FAKE, FAKE, FAKE, FAKE, 8, 16, 1 << 15, 1 << 15, FAKE, FAKE, None) == \
+        cpa.CP_ERR_OVERFLOW
 
 
 def test_binding_refuses_cpu_tensors():
