@@ -271,16 +271,18 @@ def test_allgather_packed_s32768_sampled(rank, h_q, h_kv):
         assert torch.all(out[cu[-1] - q0:] == 0)
 
 
-@pytest.mark.parametrize("ps", [2, 4, 32, 128, 256])
-def test_page_sizes(ps):
-    """Page sizes below, at and above the 64-key tile: per-lane page lookups
-    (ps < 64), one page per tile, and several tiles per page (ps > 64); pages
+@pytest.mark.parametrize("ps,d", [(2, 128), (4, 64), (8, 128), (16, 64), (32, 128), (32, 64),
+                                  (128, 128), (256, 64)])
+def test_page_sizes(ps, d):
+    """Page sizes below, at and above the 64-key tile, at both head sizes:
+    per-lane page lookups (ps < 16), whole pages per tile (ps 16 and 32),
+    and one page per tile or several tiles per page (ps >= 64); pages
     permuted; every rank of a ragged two-sequence batch, every row."""
-    w = synth.Workload(name=f"ps{ps}", seed=50 + ps, causal=True, h_q=8, h_kv=2, d=128,
+    w = synth.Workload(name=f"ps{ps}", seed=50 + ps + d, causal=True, h_q=8, h_kv=2, d=d,
                        page_size=ps, contiguous_kv=False, cp_size=3)
     lens = [1237, 419]
     for r in range(3):
         c = gc.zigzag_case(w, r, lens=lens)
         out = gc.run_attn(c)
         ref = oatt.zigzag_rank(c.q_local.cpu(), c.k_seqs, c.v_seqs, c.meta_o, c.scale)
-        gc.assert_close(out, ref, f"ps={ps} rank {r}")
+        gc.assert_close(out, ref, f"ps={ps} d={d} rank {r}")
