@@ -163,6 +163,13 @@ def test_scatter_config2_and_config3_shapes():
     assert np.array_equal(kp, k_ref) and np.array_equal(vp, v_ref)
 
 
+def test_scatter_config4_full_size():
+    """K and V of the long-context workload, [131072, 8, 128] each, into 2048
+    permuted pages of 64: the launch bench.py times, every slot bit-exact."""
+    kp, vp, k_ref, v_ref = _scatter_case(8, [131072], 8, 128, 64, seed=4, spare_pages=0)
+    assert np.array_equal(kp, k_ref) and np.array_equal(vp, v_ref)
+
+
 def test_scatter_then_attention_end_to_end():
     """Gathered K/V -> pool (scatter kernel) -> attention kernel, vs the oracle."""
     import math
