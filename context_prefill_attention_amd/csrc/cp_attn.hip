@@ -43,10 +43,11 @@
 // softmax of one 32-key block, whose VALU work is independent of that half's
 // MFMAs, so the two overlap within the wave.
 //
-// Online softmax: the running max is raised only when a probability against
-// the current one would exceed 2^8, so the O/l rescale is a rare wave-uniform
-// branch instead of 64 multiplies per block.  Row sums are accumulated in
-// fp32 from the unrounded probabilities.
+// Online softmax: probabilities are taken against a lazy reference maximum,
+// raised only when a lane's sum over one 32-key block would exceed 2^32 (or
+// is not finite), so the O/l rescale is a rare wave-uniform branch instead of
+// 64 multiplies per block.  Row sums are accumulated in fp32 from the
+// unrounded probabilities.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
