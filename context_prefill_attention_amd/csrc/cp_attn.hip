@@ -41,7 +41,9 @@
 // Software pipeline: each step handles the QK product of tile t and the PV
 // product of tile t-1, in two halves of 16 MFMAs; each half also carries the
 // softmax of one 32-key block, whose VALU work is independent of that half's
-// MFMAs, so the two overlap within the wave.
+// MFMAs, so the two overlap within the wave.  The two waves sharing a SIMD
+// meet at every step's barrier; raising a wave's issue priority during
+// half 1 lets the one that lags close the gap.
 //
 // Online softmax: probabilities are taken against a lazy reference maximum,
 // raised only when a lane's sum over one 32-key block would exceed 2^32 (or
@@ -527,9 +529,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       const Pages pg_after = fetch_pages(t + 3);
       if (t + 2 < n_pad) issue_tile(t + 2, std::integral_constant<int, (st + 2) % kStages>{}, pg_next);
       pg_next = pg_after;
+      // A wave still in half 1 outranks one already in half 2 for the
+      // SIMD's issue slots, so the wave that lags catches up before the
+      // step barrier instead of both arriving at it far apart.
+      __builtin_amdgcn_s_setprio(1);
       f32x16 s0 = qk_blk(stc, I0{});
       pv_blk(SP{}, I0{}, pk);
       sm_blk(s1, pk + 8);
+      __builtin_amdgcn_s_setprio(0);
       s1 = qk_blk(stc, I1{});
       if constexpr (MASKED) mask_blk(t, 0, s0);
       pv_blk(SP{}, I1{}, pk + 8);
