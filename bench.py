@@ -76,7 +76,16 @@ def calibrate_copy(steps: int) -> None:
                       dst.numel() * 2, "launches": steps}))
 
 
-def traffic_for(kernel_src: str, workload: str, rank: int):
+def kernel_sha256(paths) -> str:
+    """SHA-256 over the attention kernel's device sources, in order."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_for(kernel_srcs, workload: str, rank: int):
     """Measured HBM bytes per attention launch, if the committed counter
     summary was taken on this exact kernel source, workload and rank."""
     path = os.path.join(ROOT, "profiles", "attn_traffic.json")
@@ -84,7 +93,7 @@ def traffic_for(kernel_src: str, workload: str, rank: int):
         return None
     with open(path) as f:
         rec = json.load(f)
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    sha = kernel_sha256(kernel_srcs)
     if rec.get("kernel_sha256") != sha or rec.get("workload") != workload or rec.get("rank") != rank:
         return None
     return rec.get("bytes_per_launch")
@@ -198,7 +207,9 @@ def result_line(args, useful_flops: float, ms_step: float, attn_ms: float, confi
     }
 
 
-KERNEL_SRC = os.path.join(ROOT, "context_prefill_attention_amd", "csrc", "cp_attn.hip")
+# the attention kernel's device code and the table layouts it reads
+KERNEL_SRC = [os.path.join(ROOT, "context_prefill_attention_amd", "csrc", f)
+              for f in ("cp_attn_kernel.h", "cp_internal.h")]
 
 
 def run_zigzag(args, w, torch, cpa, synth) -> dict:

@@ -1,593 +1,17 @@
-// Fused zigzag context-parallel prefill attention for gfx950 (MI355X).
-//
-// One launch covers every segment of a metadata blob: both zigzag halves of
-// every sequence (causal, bottom-right aligned: row i of a q_len-row half
-// sees key j <= i + kv_len - q_len) or the AllGather-KV slice (non-causal,
-// each local query row against the keys of its own document of the ordered
-// global K/V).  Sources: sglang zigzag.py
-// source page (run_attention: the prev and next halves with their own
-// cu_seqlens_q and kv_len; build_metadata: kv_len_prev/next); the AITer GQA
-// report (KV head of query head h is h / (H_q/H_kv), scale 1/sqrt(D)); the
-// vllm-omni AllGather-KV pull request (local Q against global K/V, the pad
-// suffix is never read).
-//
-// Work decomposition.  A workgroup (8 waves, 512 lanes) owns one KV head and
-// 256 (position, query head) rows: q_tile = 256/G consecutive positions times
-// the G query heads that share the KV head, head-minor.  Every K/V tile staged
-// in LDS is therefore used by all G heads of the group.  Workgroup w takes KV
-// head w % H_kv and work item w / H_kv: consecutive workgroups are dispatched
-// round-robin over the 8 XCDs, so with H_kv in {1,2,4,8} each XCD sees one
-// KV head (or a fixed subset) and its 4 MB L2 holds that head's K/V stream.
-// Work items come longest-first from the host.
-//
-// Per wave: 32 rows.  Scores are computed transposed, S^T = K Q^T with
-// v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 d from LDS, B = Q^T held in
-// registers for the whole key loop), so lane l owns query column l%32 and
-// 16 of the 32 keys of a block; the two lane halves of a column split the
-// keys.  The probabilities are already in the B-operand layout of
-// O^T = V^T P^T, so P never leaves registers; V^T comes from LDS through
-// ds_read_b64_tr_b16.  O^T keeps each query in one lane, so the softmax and
-// its rescale are lane-local apart from one exchange between the lane halves
-// (v_permlane32_swap) per 32-key block.
-//
-// LDS: a ring of four K and V tile stages, 64 keys x D each (128 KiB at
-// D = 128), rows of D*2 bytes with the 16-byte chunk index XOR-swizzled by
-// the row so that both the K reads (16 rows, same chunk) and the transposed V
-// reads (4 rows x 4 chunks) hit distinct banks.  Tiles arrive by direct
-// global->LDS loads (global_load_lds_dwordx4) issued two tiles ahead; the
-// page ids they need are fetched three tiles ahead, so no load result is
-// waited on before the barrier that publishes its tile.
-//
-// Software pipeline: each step handles the QK product of tile t and the PV
-// product of tile t-1, in two halves of 16 MFMAs; each half also carries the
-// softmax of one 32-key block, whose VALU work is independent of that half's
-// MFMAs, so the two overlap within the wave.  The two waves sharing a SIMD
-// meet at every step's barrier; raising a wave's issue priority during
-// half 1 lets the one that lags close the gap.
-//
-// Online softmax: probabilities are taken against a lazy reference maximum,
-// raised only when a lane's sum over one 32-key block would exceed 2^32 (or
-// is not finite), so the O/l rescale is a rare wave-uniform branch instead of
-// 64 multiplies per block.  Row sums are accumulated in fp32 from the
-// unrounded probabilities.
+// Host entry point of the fused zigzag CP prefill attention (gfx950):
+// validates every argument before anything is enqueued, picks the page-id
+// mode of the kernel in cp_attn_kernel.h and launches one grid over the
+// work list of the metadata blob.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
-#include <type_traits>
 
 #include "../../include/cpattn.h"
+#include "cp_attn_kernel.h"
 #include "cp_internal.h"
 
 namespace cpattn {
 namespace {
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(4))) short i16x4;
-typedef __attribute__((ext_vector_type(8))) short i16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-
-struct AttnArgs {
-  const unsigned char* q;
-  const unsigned char* k_pool;
-  const unsigned char* v_pool;
-  unsigned char* out;
-  const Seg* segs;
-  const Work* work;
-  const int32_t* indptr;
-  const int32_t* indices;
-  int32_t h_q, h_kv, group, num_pages;
-  int32_t page_shift;
-  float scale_log2;  // softmax scale * log2(e): scores go through exp2
-};
-
-// 16-byte chunk slot of (row, chunk) inside a row of NC chunks.  For NC = 16
-// the row's low 4 bits are permuted (bits 0-1 to 2-3) and XORed into the
-// chunk: 16 consecutive rows at one chunk land in 16 different slots, and
-// 4 consecutive rows x 4 aligned chunks do too.
-template <int NC>
-__device__ __forceinline__ int swz(int row, int chunk) {
-  if constexpr (NC == 16) {
-    const int r = row & 15;
-    return chunk ^ (((r & 3) << 2) | (r >> 2));
-  } else {
-    return chunk ^ ((row >> 1) & (NC - 1));
-  }
-}
-
-__device__ __forceinline__ float wave_half_max(float x) {
-  // max of x over lanes l and l^32 (v_permlane32_swap exchanges the halves)
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float wave_half_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  f32x2 v = {a, b};
-  bf16x2 h = __builtin_convertvector(v, bf16x2);  // v_cvt_pk_bf16_f32, round to nearest even
-  return __builtin_bit_cast(uint32_t, h);
-}
-
-constexpr int kStages = 4;   // LDS ring depth (tiles); loads run two tiles ahead
-
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (lgkm and exp counters left unconstrained).
-// Encoding: vmcnt bits 3:0 and 15:14, expcnt bits 6:4, lgkmcnt bits 11:8.
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
-}
-
-// Page modes.  PM == kPageTile: pages hold >= 64 keys, a tile lies in one
-// page (or, after an unaligned segment start, two) and its id is one scalar
-// load.  PM in {16, 32}: pages of PM keys and every segment starts on a
-// page boundary, so a tile holds 64/PM whole pages whose ids are again
-// scalar loads.  PM == kPageLane (pages under 16 keys, or unaligned
-// segments): every lane looks up its own row's page with a vector load.
-constexpr int kPageLane = 0, kPageTile = 1;
-
-template <int D, int PM>
-__global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
-  constexpr int NC = D / 8;               // 16-byte chunks per K/V row
-  constexpr int KSTEPS = D / 16;          // k-steps of S^T = K Q^T
-  constexpr int DBLK = D / 32;            // 32-row blocks of O^T
-  constexpr int ROW_BYTES = D * 2;
-  constexpr int TILE_BYTES = kAttnKeys * ROW_BYTES;    // one K (or V) tile
-  constexpr int LOADS = TILE_BYTES / (kThreads * 16);  // 16-byte direct loads per lane per K (or V) tile
-  constexpr bool PAGE_PER_TILE = PM == kPageTile;
-  constexpr int GP = PM >= 16 ? PM : 0;                // page size of the group modes
-  constexpr int NPP = GP ? kAttnKeys / GP : 1;         // pages per tile in the group modes
-  constexpr int PLOADS = PM == kPageLane ? LOADS : 0;  // vector page-id loads per lane per tile
-  static_assert(LOADS >= 1 && TILE_BYTES % (kThreads * 16) == 0, "loader shape");
-  // K and V rings of kStages tiles, one array per stage: the compiler can
-  // then tell the stage being read from the stages whose direct loads are
-  // still in flight and does not wait for those loads before the read.  A
-  // direct global->LDS load writes 1 KiB per wave instruction, lane i at
-  // +16*i; the lane picks the global chunk that the swizzle puts in that slot.
-  __shared__ __attribute__((aligned(1024))) unsigned char k_s0[TILE_BYTES], k_s1[TILE_BYTES],
-      k_s2[TILE_BYTES], k_s3[TILE_BYTES], v_s0[TILE_BYTES], v_s1[TILE_BYTES], v_s2[TILE_BYTES],
-      v_s3[TILE_BYTES];
-  static_assert(kStages == 4, "one array per ring stage");
-  auto kbuf = [&](auto stc) -> unsigned char* {
-    constexpr int st = decltype(stc)::value;
-    if constexpr (st == 0) return k_s0; else if constexpr (st == 1) return k_s1;
-    else if constexpr (st == 2) return k_s2; else return k_s3;
-  };
-  auto vbuf = [&](auto stc) -> unsigned char* {
-    constexpr int st = decltype(stc)::value;
-    if constexpr (st == 0) return v_s0; else if constexpr (st == 1) return v_s1;
-    else if constexpr (st == 2) return v_s2; else return v_s3;
-  };
-
-  const int h_kv = a.h_kv, group = a.group;
-  const int kvh = blockIdx.x % h_kv;
-  const Work w = a.work[blockIdx.x / h_kv];
-  const Seg s = a.segs[w.seg];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int half = lane >> 5, col = lane & 31;
-
-  // This lane's query row: position pos of the item, query head hg of the group.
-  const int rho = wave * 32 + col;
-  const int pos = rho / group, hg = rho - pos * group;
-  const bool valid = rho < w.np * group;            // row exists in this item
-  const int qp = w.p0 + pos;                        // segment-local position
-  const bool live = valid && qp < s.q_len;          // row attends (else written as 0)
-  const int64_t qrow = (int64_t)(s.q_row0 + qp) * a.h_q + (int64_t)kvh * group + hg;
-  // Last visible key of this row; rows that do not attend use the segment's
-  // last key so that their (zero-query) scores stay finite.
-  const int limit = (s.causal && live) ? qp + s.causal_off : s.kv_len - 1;
-  // Smallest limit of the item's rows: tiles ending at or below it need no mask.
-  const int item_limit = s.causal ? w.p0 + s.causal_off : s.kv_len - 1;
-  const int n_tiles = w.n_tiles;
-  // first tile that holds a key past some row's limit
-  const int t_mask = min(n_tiles, max(0, (item_limit + 1) / kAttnKeys));
-  // Tiles the pipeline runs: n_tiles rounded up to 1 + a multiple of the
-  // ring depth (see the main loop); tiles past n_tiles hold no visible key.
-  const int n_pad = n_tiles > 0 ? 1 + ((n_tiles + 2) & ~3) : 0;
-
-  bf16x8 qop[KSTEPS];
-#pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    if (live) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(a.q + (qrow * D + ks * 16 + half * 8) * 2);
-      qop[ks] = __builtin_bit_cast(bf16x8, v);
-    } else {
-      qop[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-    }
-  }
-
-  // Loader geometry: direct load u of this lane writes LDS byte
-  // (u*8 + wave)*1024 + 16*lane of the tile, i.e. one 16-byte slot of key row
-  // ld_row[u]; it fetches the chunk that the swizzle places in that slot.
-  // The page table is read-only for the whole kernel: read it through the
-  // constant address space so that wave-uniform lookups become scalar loads.
-  typedef const __attribute__((address_space(4))) int32_t cint32;
-  cint32* ptab = (cint32*)(a.indices) + a.indptr[s.page_row];
-  const int shift = a.page_shift;
-  const int ps_mask = (1 << shift) - 1;
-  const uint32_t tok_stride = (uint32_t)h_kv * ROW_BYTES;
-  // Key j of the segment is position kv0 + j of its page-table row (kv0 > 0
-  // for all but the first document of a packed AllGather-KV slice).  When kv0
-  // is not a multiple of the tile size, a tile may straddle two pages.
-  const int kv0 = s.kv_start;
-  const bool straddle = (kv0 & (kAttnKeys - 1)) != 0;
-  const int n_entries = a.indptr[s.page_row + 1] - a.indptr[s.page_row];
-  int ld_row[LOADS];
-  uint32_t ld_lane[LOADS];   // chunk offset from the head-0 start of the lane's token row
-#pragma unroll
-  for (int u = 0; u < LOADS; ++u) {
-    const int o = (u * kWaves + wave) * 1024 + lane * 16;
-    const int row = o / ROW_BYTES, slot = (o % ROW_BYTES) / 16;
-    ld_row[u] = row;
-    ld_lane[u] = (uint32_t)(kvh * ROW_BYTES + swz<NC>(row, slot) * 16);  // swz is an involution
-  }
-  // Every tile issues exactly LOADS direct loads of K and LOADS of V per
-  // lane (and, with small pages, LOADS page-id loads), whatever the row: rows
-  // past kv_len or with a page id outside the pool are redirected to key 0 of
-  // the sequence (always real and finite) and masked out of the scores.  The
-  // per-wave vector-memory counts are then exact and the waits below can
-  // leave the younger tiles in flight.
-  // With pages of >= 64 keys: the page of the tile's first key and, if the
-  // tile may straddle a page boundary, the next one.
-  // Group modes: the tile's NPP pages as scalars (pg.p[j] = page of keys
-  // j*GP .. j*GP+GP-1 of the tile); lane lookups: the page of each of this
-  // lane's rows.
-  constexpr int NPG = PAGE_PER_TILE ? 2 : (GP != 0 ? NPP : LOADS);
-  struct Pages { int p[NPG]; };
-  auto fetch_pages = [&](int t) -> Pages {
-    Pages pg;
-    if constexpr (PAGE_PER_TILE) {
-      const int e0 = (kv0 + min(t, n_tiles - 1) * kAttnKeys) >> shift;
-      pg.p[0] = ptab[e0];
-      pg.p[1] = straddle ? ptab[min(e0 + 1, n_entries - 1)] : pg.p[0];
-    } else if constexpr (GP != 0) {
-      const int e0 = (kv0 + min(t, n_tiles - 1) * kAttnKeys) >> shift;
-#pragma unroll
-      for (int j = 0; j < NPP; ++j) pg.p[j] = ptab[min(e0 + j, n_entries - 1)];
-    } else {
-#pragma unroll
-      for (int u = 0; u < LOADS; ++u) {
-        const int key = max(0, min(t * kAttnKeys + ld_row[u], s.kv_len - 1));
-        pg.p[u] = ptab[(kv0 + key) >> shift];
-      }
-    }
-    return pg;
-  };
-  const int page0 = ptab[0];
-  const bool page0_ok = page0 >= 0 && page0 < a.num_pages;
-  // Per-lane part of a load address when a whole tile lies in one page.
-  uint32_t ld_const[LOADS];
-#pragma unroll
-  for (int u = 0; u < LOADS; ++u) ld_const[u] = (uint32_t)ld_row[u] * tok_stride + ld_lane[u];
-  auto issue_tile = [&](int t, auto stc, const Pages& pg) {
-    unsigned char* kd = kbuf(stc);
-    unsigned char* vd = vbuf(stc);
-    // Common case (a tile within one page): every key of the tile is real
-    // and its page id valid, so each address is a wave-uniform base plus a
-    // per-lane constant.
-    const int first = kv0 + t * kAttnKeys;   // page-table position of the tile's key 0
-    if (PAGE_PER_TILE && (t + 1) * kAttnKeys <= s.kv_len && pg.p[0] >= 0 && pg.p[0] < a.num_pages &&
-        (first & ps_mask) + kAttnKeys <= ps_mask + 1) {
-      const uint64_t base =
-          (((uint64_t)pg.p[0] << shift) | (uint32_t)(first & ps_mask)) * tok_stride;
-#pragma unroll
-      for (int u = 0; u < LOADS; ++u) {
-        __builtin_amdgcn_global_load_lds(a.k_pool + (int64_t)(base + ld_const[u]),
-            (__attribute__((address_space(3))) void*)&kd[(u * kWaves + wave) * 1024], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(a.v_pool + (int64_t)(base + ld_const[u]),
-            (__attribute__((address_space(3))) void*)&vd[(u * kWaves + wave) * 1024], 16, 0, 0);
-      }
-      return;
-    }
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int key = t * kAttnKeys + ld_row[u];
-      const int pos = kv0 + key;
-      int page;
-      if constexpr (PAGE_PER_TILE) {
-        page = (pos >> shift) == (first >> shift) ? pg.p[0] : pg.p[1];
-      } else if constexpr (GP != 0) {
-        // Page j = ld_row[u] / GP of the tile holds this lane's row, chosen
-        // by a tree of selects on the bits of j (a flat compare chain would
-        // be turned into an indexed array in memory).
-        const int j = ld_row[u] / GP;
-        static_assert(NPP == 2 || NPP == 4, "group modes hold 2 or 4 pages per tile");
-        const int q0 = pg.p[0] ^ ((pg.p[0] ^ pg.p[1]) & -(j & 1));
-        if constexpr (NPP == 2) {
-          page = q0;
-        } else {
-          const int q1 = (j & 1) ? pg.p[3] : pg.p[2];
-          page = (j & 2) ? q1 : q0;
-        }
-      } else {
-        page = pg.p[u];
-      }
-      const bool ok = key < s.kv_len && page >= 0 && page < a.num_pages;
-      const int64_t tok = ok ? ((int64_t)page << shift | (pos & ps_mask))
-                             : (page0_ok ? (int64_t)page0 << shift : 0);
-      const int64_t off = tok * tok_stride + ld_lane[u];
-      __builtin_amdgcn_global_load_lds(a.k_pool + off,
-          (__attribute__((address_space(3))) void*)&kd[(u * kWaves + wave) * 1024], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(a.v_pool + off,
-          (__attribute__((address_space(3))) void*)&vd[(u * kWaves + wave) * 1024], 16, 0, 0);
-    }
-  };
-  // Wait until tile t's direct loads have landed, given what this wave
-  // issued after them: the page ids of tile t+2 (with small pages) and the
-  // loads of tile t+1, if those tiles exist.
-  auto wait_tile = [&](int t) {
-    if (PLOADS != 0 && t + 2 < n_pad) wait_vmcnt<PLOADS + 2 * LOADS>();
-    else if (t + 1 < n_pad) wait_vmcnt<2 * LOADS>();
-    else wait_vmcnt<0>();
-  };
-
-  // LDS read offsets of this lane, fixed for the whole loop (stage, block
-  // and step offsets are immediates):
-  //   K: key row kb*32 + col, chunk 2*ks + half       (kb adds 32 rows)
-  //   V: key row 16*st + 8*e + 4*half + j/4, chunk 4*db + 2*gsub + (j%4)/2,
-  //      8-byte half j%2                              (st adds 16 rows)
-  // 16 rows do not change the swizzle, so both row offsets are additive.
-  uint32_t kofs[KSTEPS], vofs[DBLK][2];
-  {
-    const int j = lane & 15, gsub = (lane >> 4) & 1;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) kofs[ks] = col * ROW_BYTES + swz<NC>(col, ks * 2 + half) * 16;
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int row = 8 * e + half * 4 + (j >> 2);
-        const int chunk = db * 4 + gsub * 2 + ((j & 3) >> 1);
-        vofs[db][e] = row * ROW_BYTES + swz<NC>(row, chunk) * 16 + (j & 1) * 8;
-      }
-  }
-
-  f32x16 o[DBLK];
-#pragma unroll
-  for (int i = 0; i < DBLK; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const float c = a.scale_log2;
-  // Rescale threshold: the running max is only raised when a lane's sum of
-  // one block's probabilities against the current reference exceeds 2^32, so
-  // O and l are rescaled rarely (the result is the same softmax with another
-  // reference).
-  constexpr float kSumLimit = 4294967296.f;
-
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-
-  // S^T of key block kb (keys 32*kb .. 32*kb+31) of the tile in stage st:
-  // KSTEPS MFMAs over d, K from LDS, Q^T from registers.
-  auto qk_blk = [&](auto stc, auto kbc) -> f32x16 {
-    constexpr int kb = decltype(kbc)::value;
-    const unsigned char* kt = kbuf(stc) + kb * 32 * ROW_BYTES;
-    f32x16 acc = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(kt + kofs[ks]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qop[ks], acc, 0, 0, 0);
-    }
-    return acc;
-  };
-  // O^T += V^T P^T over key block kb of the tile in stage st, P of that
-  // block in pb (8 registers of packed bf16 pairs, C-element order).  Two
-  // 16-key steps; step kk uses C elements 8*kk .. 8*kk+7 of the block, i.e.
-  // keys 32*kb + 16*kk + 8*(i/4) + 4*half + i%4 for operand slot i.
-  auto pv_blk = [&](auto stc, auto kbc, const uint32_t* pb) {
-    constexpr int kb = decltype(kbc)::value;
-    unsigned char* vt = vbuf(stc);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int kst = kb * 2 + kk;
-      const uint32_t* pp = pb + kk * 4;
-      const bf16x8 pop = __builtin_bit_cast(bf16x8, u32x4{pp[0], pp[1], pp[2], pp[3]});
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)((__attribute__((address_space(3))) unsigned char*)vt + vofs[db][0] + kst * 16 * ROW_BYTES));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)((__attribute__((address_space(3))) unsigned char*)vt + vofs[db][1] + kst * 16 * ROW_BYTES));
-        const i16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pop, o[db], 0, 0, 0);
-      }
-    }
-  };
-  // Keys of block kb of tile t past each row's limit leave the scores.
-  auto mask_blk = [&](int t, int kb, f32x16& sb) {
-    const int rel = limit - t * kAttnKeys - kb * 32 - half * 4;   // visible key offsets within the block
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if ((j >> 2) * 8 + (j & 3) > rel) sb[j] = -INFINITY;
-  };
-  // Probabilities of one block against reference mr (exp2 domain), packed to
-  // bf16 pairs in pb; returns their fp32 sum.
-  auto probs_blk = [&](const f32x16& sb, float mr, uint32_t* pb) -> float {
-    const float mc = mr * c;
-    float r0 = 0.f, r1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; j += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[j], c, -mc));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[j + 1], c, -mc));
-      pb[j >> 1] = pack_bf16x2(p0, p1);
-      r0 += p0;
-      r1 += p1;
-    }
-    return r0 + r1;
-  };
-  // Online softmax of one 32-key block with a lazy reference: probabilities
-  // against the current reference; if some lane's block sum exceeds 2^32 (or
-  // is not finite), the rare raise of that wave's references to their rows'
-  // maxima.  A raise rescales O and l, which at that point hold only terms
-  // taken with the old reference, and recomputes this block's probabilities;
-  // every other block's P has either been added to O already or is computed
-  // later.  The test reads the sums themselves, so the common path stays one
-  // basic block.  Between raises every probability stays below 2^32, far
-  // from fp32 overflow in O and l.
-  auto sm_blk = [&](const f32x16& sb, uint32_t* pb) {
-    const float mc = m_run * c;
-    float r0 = 0.f, r1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; j += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[j], c, -mc));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[j + 1], c, -mc));
-      pb[j >> 1] = pack_bf16x2(p0, p1);
-      r0 += p0;
-      r1 += p1;
-    }
-    float rs = r0 + r1;
-    if (__builtin_amdgcn_ballot_w64(!(rs <= kSumLimit)) != 0) {   // rare: raise the references
-      // The first pass's results count as used here, so the compiler keeps
-      // that pass ahead of the branch, next to the MFMAs it overlaps, rather
-      // than sinking it into the common path (which also splits O's
-      // registers into two copies).
-      asm volatile("" ::"v"(rs));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) asm volatile("" ::"v"(pb[j]));
-      float mx = sb[0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sb[j]);
-      mx = wave_half_max(mx);
-      const float m_new = fmaxf(m_run, mx);   // rows whose max did not grow keep theirs
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-      rs = probs_blk(sb, m_new, pb);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
-      m_run = m_new;
-    }
-    l_run += rs;
-  };
-
-  // Barrier between pipeline steps: this wave's LDS reads are complete, the
-  // direct loads of the tile the next step computes have landed (the caller's
-  // vmcnt wait), and no wave passes until all have.  A plain s_barrier: the
-  // usual __syncthreads would also wait for the younger tiles still in flight.
-  auto step_barrier = [&]() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
-
-  // Pipeline.  Tile t lives in ring stage t % 4.  Step t issues the page ids
-  // of tile t+3 and the loads of tile t+2, then runs two halves, each one
-  // basic block in which MFMAs and the softmax VALU work are independent:
-  //   half 1: S^T block 0 of tile t, PV of block 0 of tile t-1, softmax of
-  //           block 1 of tile t-1;
-  //   half 2: S^T block 1 of tile t, PV of block 1 of tile t-1, softmax of
-  //           block 0 of tile t.
-  // The barrier at the end of step t publishes tile t+1 and retires every
-  // read of tile t-1's stage, which step t+1 refills with tile t+3.
-  // Between steps, s1 holds S^T block 1 of the last tile and pk[0..7] the
-  // probabilities of its block 0; pk[8..15] hold block 1's once computed.
-  uint32_t pk[16];
-  if (n_tiles > 0) {
-    Pages pg0 = fetch_pages(0), pg1 = fetch_pages(1);
-    issue_tile(0, I0{}, pg0);
-    Pages pg_next = fetch_pages(2);
-    if (n_pad > 1) issue_tile(1, I1{}, pg1);
-    wait_tile(0);
-    step_barrier();
-
-    f32x16 s1;
-    // Step 0: no previous tile.
-    {
-      const Pages pg_after = fetch_pages(3);
-      if (2 < n_pad) issue_tile(2, I2{}, pg_next);
-      pg_next = pg_after;
-      f32x16 s0 = qk_blk(I0{}, I0{});
-      s1 = qk_blk(I0{}, I1{});
-      if (t_mask == 0) {
-        mask_blk(0, 0, s0);
-        mask_blk(0, 1, s1);
-      }
-      sm_blk(s0, pk);
-      wait_tile(1);
-      step_barrier();
-    }
-
-    // Step t >= 1; MASKED tiles hold keys past some row's limit.
-    auto step = [&](auto stc, auto maskc, int t) {
-      constexpr int st = decltype(stc)::value;   // t % kStages
-      constexpr bool MASKED = decltype(maskc)::value;
-      using SP = std::integral_constant<int, (st + kStages - 1) % kStages>;   // stage of tile t-1
-      const Pages pg_after = fetch_pages(t + 3);
-      if (t + 2 < n_pad) issue_tile(t + 2, std::integral_constant<int, (st + 2) % kStages>{}, pg_next);
-      pg_next = pg_after;
-      // A wave still in half 1 outranks one already in half 2 for the
-      // SIMD's issue slots, so the wave that lags catches up before the
-      // step barrier instead of both arriving at it far apart.
-      __builtin_amdgcn_s_setprio(1);
-      f32x16 s0 = qk_blk(stc, I0{});
-      pv_blk(SP{}, I0{}, pk);
-      sm_blk(s1, pk + 8);
-      __builtin_amdgcn_s_setprio(0);
-      s1 = qk_blk(stc, I1{});
-      if constexpr (MASKED) mask_blk(t, 0, s0);
-      pv_blk(SP{}, I1{}, pk + 8);
-      sm_blk(s0, pk);
-      if constexpr (MASKED) mask_blk(t, 1, s1);
-      wait_tile(t + 1);
-      step_barrier();
-    };
-
-    int t = 1;
-    const int t_full_end = max(1, t_mask);          // tiles [1, t_mask) need no mask
-    // Both loops are unrolled by the ring depth, so every stage index is a
-    // constant and each loop body is a single path.  After the first, t % 4
-    // == 1; the second runs the remaining tiles (a few fully visible ones,
-    // which the mask leaves unchanged, then the diagonal) up to n_pad, and
-    // its padding tiles are fully masked.  The last tile, n_pad - 1, is then
-    // always in stage 0.
-    for (; t + 3 < t_full_end; t += 4) {
-      step(I1{}, std::false_type{}, t);
-      step(I2{}, std::false_type{}, t + 1);
-      step(I3{}, std::false_type{}, t + 2);
-      step(I0{}, std::false_type{}, t + 3);
-    }
-    for (; t < n_pad; t += 4) {
-      step(I1{}, std::true_type{}, t);
-      step(I2{}, std::true_type{}, t + 1);
-      step(I3{}, std::true_type{}, t + 2);
-      step(I0{}, std::true_type{}, t + 3);
-    }
-    // The last tile's PV products and its block-1 softmax.
-    pv_blk(I0{}, I0{}, pk);
-    sm_blk(s1, pk + 8);
-    pv_blk(I0{}, I1{}, pk + 8);
-  }
-
-  // Epilogue: O = O^T / l.  Lane (col, half) holds d = 32*db + 8*(j/4) + 4*half + j%4.
-  if (!valid) return;
-  const float l_tot = wave_half_sum(l_run);   // the two lane halves summed different keys
-  const float inv = live ? 1.f / l_tot : 0.f;
-  unsigned char* orow = a.out + qrow * D * 2;
-#pragma unroll
-  for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int d = db * 32 + jj * 8 + half * 4;
-      u32x2 v;
-      v[0] = pack_bf16x2(o[db][jj * 4 + 0] * inv, o[db][jj * 4 + 1] * inv);
-      v[1] = pack_bf16x2(o[db][jj * 4 + 2] * inv, o[db][jj * 4 + 3] * inv);
-      *reinterpret_cast<u32x2*>(orow + d * 2) = v;
-    }
-}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -613,6 +37,9 @@ extern "C" int cp_prefill_attn(const void* q, const void* k_pool, const void* v_
     return set_error(CP_ERR_INVALID_ARG, "metadata work list was built for H_q/H_kv=%d, not %d",
                      meta->attn_group, H_q / H_kv);
   if (D != 64 && D != 128) return set_error(CP_ERR_UNSUPPORTED, "D=%d (supported: 64, 128)", D);
+  // A lane's load offset inside one 64-key tile is kept in 32 bits.
+  if ((int64_t)H_kv * D * 2 * kAttnKeys > 2147483647LL)
+    return set_error(CP_ERR_UNSUPPORTED, "H_kv=%d is too many KV heads for D=%d", H_kv, D);
   if (!(scale > 0.f) || !std::isfinite(scale))
     return set_error(CP_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (page_size < 1 || (page_size & (page_size - 1)) != 0 || page_size > (1 << 20))

@@ -241,8 +241,9 @@ int cp_kv_scatter(const void* d_blob, const cp_meta_t* meta,
  *     kv_align overstates the segments' alignment gives unspecified results,
  *     again with no out-of-bounds read.  The meta builders set it exactly.
  * Requires H_q % H_kv == 0 (else CP_ERR_INVALID_ARG, [P4]), H_q/H_kv equal to
- * meta->attn_group, D in {64, 128}, page_size a power of two, scale finite
- * and > 0.
+ * meta->attn_group, D in {64, 128}, H_kv*D*2*64 < 2^31 (one 64-key tile of
+ * all KV heads; else CP_ERR_UNSUPPORTED), page_size a power of two, scale
+ * finite and > 0.
  */
 int cp_prefill_attn(const void* q, const void* k_pool, const void* v_pool, void* out,
                     int32_t H_q, int32_t H_kv, int32_t D, float scale,

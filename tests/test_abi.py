@@ -274,6 +274,8 @@ def test_attention_validation_fails_closed(lib):
     assert b"multiple" in lib.cp_last_error()
     assert _attn(lib, m, h_q=32, h_kv=32) == cpa.CP_ERR_INVALID_ARG       # list built for G=8
     assert _attn(lib, m, d=96) == cpa.CP_ERR_UNSUPPORTED
+    m_big = cpa.meta_build(2, 0, [64], attn_group=1)
+    assert _attn(lib, m_big, h_q=1 << 18, h_kv=1 << 18) == cpa.CP_ERR_UNSUPPORTED   # 64 rows pass 2^31 bytes
     assert _attn(lib, m, scale=0.0) == cpa.CP_ERR_INVALID_ARG
     assert _attn(lib, m, scale=float("nan")) == cpa.CP_ERR_INVALID_ARG
     assert _attn(lib, m, ps=24) == cpa.CP_ERR_UNSUPPORTED

@@ -54,15 +54,17 @@ def test_causal_pairs_of_the_long_share():
 
 
 def test_traffic_reported_only_for_its_source_workload_and_rank(tmp_path, monkeypatch):
-    src = tmp_path / "k.hip"
+    src = tmp_path / "k.h"
     src.write_text("kernel source")
-    sha = hashlib.sha256(b"kernel source").hexdigest()
+    inc = tmp_path / "tables.h"
+    inc.write_text("tables")
+    sha = hashlib.sha256(b"kernel sourcetables").hexdigest()
     (tmp_path / "profiles").mkdir()
     rec = {"kernel_sha256": sha, "workload": "long_cp8_s131072_r3", "rank": 3, "bytes_per_launch": 123}
     (tmp_path / "profiles" / "attn_traffic.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    assert bench.traffic_for(str(src), "long_cp8_s131072_r3", 3) == 123
-    assert bench.traffic_for(str(src), "long_cp8_s131072_r3", 2) is None
-    assert bench.traffic_for(str(src), "gqa_cp2_s8192", 3) is None
+    assert bench.traffic_for([str(src), str(inc)], "long_cp8_s131072_r3", 3) == 123
+    assert bench.traffic_for([str(src), str(inc)], "long_cp8_s131072_r3", 2) is None
+    assert bench.traffic_for([str(src), str(inc)], "gqa_cp2_s8192", 3) is None
     src.write_text("kernel source, changed")
-    assert bench.traffic_for(str(src), "long_cp8_s131072_r3", 3) is None
+    assert bench.traffic_for([str(src), str(inc)], "long_cp8_s131072_r3", 3) is None
