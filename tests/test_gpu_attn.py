@@ -286,3 +286,61 @@ def test_page_sizes(ps, d):
         out = gc.run_attn(c)
         ref = oatt.zigzag_rank(c.q_local.cpu(), c.k_seqs, c.v_seqs, c.meta_o, c.scale)
         gc.assert_close(out, ref, f"ps={ps} d={d} rank {r}")
+
+
+def _sweep_params(seed):
+    """Random small shapes: cp, ragged lengths, optional cached prefixes, head
+    groups, head size and page size (every page mode), drawn from the seed."""
+    rng = np.random.default_rng(1000 + seed)
+    cp = int(rng.choice([2, 3, 4, 5, 8]))
+    bs = int(rng.integers(1, 4))
+    lens = [int(rng.integers(2 * cp, 2 * cp + 300)) for _ in range(bs)]
+    prefix = [int(rng.integers(0, 200)) if rng.random() < 0.4 else 0 for _ in range(bs)]
+    h_kv = int(rng.choice([1, 2, 4]))
+    group = int(rng.choice([1, 2, 3, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    ps = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 128]))
+    return cp, lens, prefix, h_kv * group, h_kv, d, ps
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_zigzag_sweep_all_ranks_all_rows(seed):
+    """Seeded random shapes through the whole causal path, every rank and row."""
+    cp, lens, prefix, h_q, h_kv, d, ps = _sweep_params(seed)
+    print("sweep", seed, "cp", cp, "lens", lens, "prefix", prefix, "heads", h_q, h_kv, "d", d, "ps", ps,
+          flush=True)
+    _prefix_extend_case(cp, lens, prefix, h_q, h_kv, d, ps, 500 + seed)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_packed_allgather_sweep(seed):
+    """Seeded random packed AllGather-KV slices: document lengths (some
+    page-aligned, some not), pad suffix, degree, heads, head and page size;
+    every rank, every row."""
+    rng = np.random.default_rng(2000 + seed)
+    ps = int(rng.choice([4, 16, 32, 64]))
+    a = int(rng.choice([2, 3, 4]))
+    m = int(np.lcm(a, ps))     # the slices split evenly and the pool holds whole pages
+    kv_total = m * int(rng.integers(max(2, 48 // m), max(3, 640 // m)))
+    align = ps if rng.random() < 0.5 else 1
+    cu = [0]
+    while True:
+        n = align * int(rng.integers(1, max(2, 200 // align)))
+        if cu[-1] + n >= kv_total:
+            break
+        cu.append(cu[-1] + n)
+    if rng.random() < 0.5 or len(cu) == 1:
+        cu.append(kv_total - int(rng.integers(0, min(40, kv_total // 4))))
+    h_kv = int(rng.choice([1, 2]))
+    h_q = h_kv * int(rng.choice([1, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    share = kv_total // a
+    print("packed sweep", seed, "cu", cu, "kv_total", kv_total, "a", a, "heads", h_q, h_kv, "d", d, "ps", ps,
+          flush=True)
+    for r in range(a):
+        q, kg, vg, out, scale = _packed_run(cu, r * share, share, h_q, h_kv, d, ps, kv_total, 3000 + seed,
+                                            permute=True)
+        ref = oatt.allgather_kv_packed(q, kg, vg, cu, r * share, scale)
+        gc.assert_close(out, ref, f"packed sweep {seed} rank {r}")
+        pad0 = max(0, cu[-1] - r * share)
+        assert torch.all(out[pad0:] == 0)
