@@ -298,3 +298,11 @@ def test_allgather_packed_document_order_invariance():
         cu2.append(cu2[-1] + lens[b])
     o2 = oatt.allgather_kv_packed(q2, k2, v2, cu2, 0, scale=0.7)
     assert np.max(np.abs(o2 - np.concatenate([o[s] for s in segs]))) < 1e-14
+
+
+def test_default_scale_values():
+    """head_size ** -0.5 ([P4]) at head sizes where it is exact in binary."""
+    assert oatt.default_scale(64) == 0.125
+    assert oatt.default_scale(16) == 0.25
+    assert oatt.default_scale(256) == 0.0625
+    assert abs(oatt.default_scale(128) ** 2 * 128 - 1.0) < 1e-15

@@ -105,3 +105,19 @@ def test_scatter_writes_every_real_token_and_nothing_else():
                                               m.prefix_offsets[b] + m.extend_lens[b])
             assert np.array_equal(seqrows[m.prefix_offsets[b]:], x[start:start + m.extend_lens[b]])
             start += m.extend_lens[b]
+
+
+def test_strip_pads_tiny_layout_by_hand():
+    """cp 2, one sequence of 6 tokens: blocks [2, 2, 1, 1]; rank 0 holds blocks
+    0 and 3 (tokens 0, 1, 5), rank 1 blocks 1 and 2 (tokens 2, 3, 4), so
+    max_rank_len = 3 and nothing is padded; with 7 tokens (blocks [2, 2, 2, 1])
+    rank 0 holds 0, 1, 6 and rank 1 holds 2, 3, 4, 5: rank 0 gets one pad row."""
+    m6 = zigzag_meta.build(2, 0, 6)
+    x6 = np.arange(6)
+    g6 = layout.gathered_buffer(x6, m6, pad_value=-1)
+    assert g6.tolist() == [0, 1, 5, 2, 3, 4]
+    assert layout.strip_pads(g6, m6).tolist() == [0, 1, 5, 2, 3, 4]
+    m7 = zigzag_meta.build(2, 0, 7)
+    g7 = layout.gathered_buffer(np.arange(7), m7, pad_value=-1)
+    assert g7.tolist() == [0, 1, 6, -1, 2, 3, 4, 5]
+    assert layout.strip_pads(g7, m7).tolist() == [0, 1, 6, 2, 3, 4, 5]

@@ -190,3 +190,18 @@ def test_segments_cover_local_rows_in_order():
                 assert r0 == row
                 row += q_len
             assert row == m.per_rank_actual_token[r]
+
+
+@pytest.mark.parametrize("cp,ntok,lens,ok", [
+    (2, 4, [4], True),            # exactly 2*cp tokens: one token per block
+    (2, 3, [3], False),           # one block would be empty
+    (4, 64, [8, 56], True),
+    (4, 64, [7, 57], False),      # the first sequence is one token short
+    (1, 100, [100], False),       # a single rank is not context parallel
+    (3, 6, None, True),           # no per-sequence lengths: only the batch total counts
+    (3, 5, None, False),
+])
+def test_can_apply_boundaries(cp, ntok, lens, ok):
+    """The zigzag strategy's applicability ([P5] can_apply) at its exact
+    boundaries: every one of the 2*cp blocks must get at least one token."""
+    assert zigzag_meta.can_apply(cp, ntok, lens) is ok
