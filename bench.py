@@ -269,8 +269,10 @@ def run_zigzag(args, w, torch, cpa, synth) -> dict:
     res.update({
         "rerange_kv_ms": round(ph["rerange"], 4),
         "rerange_gbps": round(rerange_bytes / (ph["rerange"] * 1e-3) / 1e9, 1),
+        "rerange_frac_of_hbm_peak": round(rerange_bytes / (ph["rerange"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "scatter_kv_ms": round(ph["scatter"], 4),
         "scatter_gbps": round(scatter_bytes / (ph["scatter"] * 1e-3) / 1e9, 1),
+        "scatter_frac_of_hbm_peak": round(scatter_bytes / (ph["scatter"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "roofline": roofline,
     })
     if not args.no_cpu_baseline:
