@@ -155,7 +155,6 @@ def test_scatter_bit_exact_with_sentinels(cp, lens, h_kv, d, ps, seq):
 
 
 def test_scatter_config2_and_config3_shapes():
-    _kp, _vp, k_ref, v_ref = None, None, None, None
     kp, vp, k_ref, v_ref = _scatter_case(2, [8192], 4, 128, 16, seed=2, spare_pages=0)
     assert np.array_equal(kp, k_ref) and np.array_equal(vp, v_ref)
     lens = synth.sequence_lengths(synth.WORKLOADS["varlen_cp4_bs8"])
