@@ -164,20 +164,23 @@ def cpu_baseline_allgather(w, h_q, q_loc, k_g, v_g, doc_cu, q_start, n_rows: int
 def run_timed(torch, step, names, warmup: int, steps: int):
     """Run ``warmup`` untimed steps, then ``steps`` timed ones.  step(ev)
     records ev[i] before phase names[i] and ev[-1] after the last phase (ev
-    is None when untimed).  Returns (wall ms per step, {phase: mean ms})."""
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-    acc = dict.fromkeys(names, 0.0)
+    is None when untimed).  Every timed step has its own events, so the host
+    prepares the next step while the GPU runs this one; the device is
+    synchronised only around the timed region.  Returns (wall ms per step,
+    {phase: mean ms})."""
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        step(ev)
-        torch.cuda.synchronize()   # per step, so the events of every step can be read
-        for i, n in enumerate(names):
-            acc[n] += ev[i].elapsed_time(ev[i + 1])
+    for k in range(steps):
+        step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    acc = dict.fromkeys(names, 0.0)
+    for ev in evs:
+        for i, n in enumerate(names):
+            acc[n] += ev[i].elapsed_time(ev[i + 1])
     return wall * 1e3 / steps, {n: v / steps for n, v in acc.items()}
 
 
