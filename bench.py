@@ -133,6 +133,32 @@ def cpu_baseline(w, meta_lists, q_loc, k_seq, v_seq, n_rows: int):
                       f"of the same rank share, all visible keys, numpy float64; {dt:.1f} s"}
 
 
+def cpu_baseline_copies(w, rank, lens, k_g, indptr, indices, n_pages):
+    """Time the oracle's metadata (pure Python), its rerange and its KV
+    scatter (numpy row copies) on K of the same share; GB/s as the device
+    copies count them (each row read once and written once)."""
+    import numpy as np
+    from oracle import layout, zigzag_meta
+    total = sum(lens)
+    t0 = time.perf_counter()
+    mo = zigzag_meta.build(w.cp_size, rank, total, extend_lens=lens)
+    meta_s = time.perf_counter() - t0
+    gathered = k_g.view(__import__("torch").int16).numpy()
+    row_bytes = w.h_kv * w.d * 2
+    t0 = time.perf_counter()
+    layout.rerange(gathered, mo)
+    rer_s = time.perf_counter() - t0
+    pool = np.zeros((n_pages, w.page_size, w.h_kv, w.d), dtype=np.int16)
+    t0 = time.perf_counter()
+    layout.kv_scatter(gathered, mo, pool, indptr, indices, w.page_size)
+    sc_s = time.perf_counter() - t0
+    moved = 2 * total * row_bytes
+    return {"meta_ms": round(meta_s * 1e3, 3), "rerange_gbps": round(moved / rer_s / 1e9, 2),
+            "scatter_gbps": round(moved / sc_s / 1e9, 2), "cores": 1, "kind": "oracle",
+            "sample": f"K of the same share ({total} rows of {row_bytes} B): zigzag_meta.build, "
+                      f"layout.rerange and layout.kv_scatter; {meta_s + rer_s + sc_s:.1f} s"}
+
+
 def cpu_baseline_allgather(w, h_q, q_loc, k_g, v_g, doc_cu, q_start, n_rows: int, packed: bool):
     """Time the fp64 oracle on evenly spaced local query rows of the
     AllGather-KV share; scale to useful TFLOP/s."""
@@ -167,7 +193,7 @@ def run_timed(torch, step, names, warmup: int, steps: int):
     is None when untimed).  Every timed step has its own events, so the host
     prepares the next step while the GPU runs this one; the device is
     synchronised only around the timed region.  Returns (wall ms per step,
-    {phase: mean ms})."""
+    {phase: mean ms}, {phase: [ms of every step]})."""
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
     for _ in range(warmup):
         step(None)
@@ -177,11 +203,8 @@ def run_timed(torch, step, names, warmup: int, steps: int):
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    acc = dict.fromkeys(names, 0.0)
-    for ev in evs:
-        for i, n in enumerate(names):
-            acc[n] += ev[i].elapsed_time(ev[i + 1])
-    return wall * 1e3 / steps, {n: v / steps for n, v in acc.items()}
+    per = {n: [ev[i].elapsed_time(ev[i + 1]) for ev in evs] for i, n in enumerate(names)}
+    return wall * 1e3 / steps, {n: sum(v) / steps for n, v in per.items()}, per
 
 
 def result_line(args, useful_flops: float, ms_step: float, attn_ms: float, config: dict,
@@ -202,6 +225,7 @@ def result_line(args, useful_flops: float, ms_step: float, attn_ms: float, confi
         "data": "synthetic",
         "config": config,
         "attn_ms": round(attn_ms, 4),
+        "attn_ms_median": None,
         "attn_useful_tflops": round(attn_tflops, 2),
         "attn_frac_of_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
@@ -259,7 +283,7 @@ def run_zigzag(args, w, torch, cpa, synth) -> dict:
         if ev:
             ev[3].record()
 
-    ms_step, ph = run_timed(torch, step, ["scatter", "rerange", "attn"], args.warmup, args.steps)
+    ms_step, ph, per = run_timed(torch, step, ["scatter", "rerange", "attn"], args.warmup, args.steps)
     if not torch.isfinite(out).all():
         print("non-finite attention output", file=sys.stderr)
         sys.exit(1)
@@ -268,6 +292,7 @@ def run_zigzag(args, w, torch, cpa, synth) -> dict:
               "page_size": w.page_size, "parallelism": "one CP rank's share on one GPU"}
     res = result_line(args, useful_flops, ms_step, ph["attn"], config,
                       traffic_for(KERNEL_SRC, w.name, rank))
+    res["attn_ms_median"] = round(float(sorted(per["attn"])[len(per["attn"]) // 2]), 4)
     roofline = res.pop("roofline")
     res.update({
         "rerange_kv_ms": round(ph["rerange"], 4),
@@ -283,6 +308,7 @@ def run_zigzag(args, w, torch, cpa, synth) -> dict:
         # timing does not depend on the values)
         res["cpu_baseline"] = cpu_baseline(w, {"segments": segs}, q_loc, k_g[:total], v_g[:total],
                                            args.cpu_rows)
+        res["cpu_baseline_copies"] = cpu_baseline_copies(w, rank, lens, k_g, indptr, indices, n_pages)
     return res
 
 
@@ -332,7 +358,7 @@ def run_allgather(args, w, torch, cpa, synth) -> dict:
         if ev:
             ev[1].record()
 
-    ms_step, ph = run_timed(torch, step, ["attn"], args.warmup, args.steps)
+    ms_step, ph, per = run_timed(torch, step, ["attn"], args.warmup, args.steps)
     if not torch.isfinite(out).all():
         print("non-finite attention output", file=sys.stderr)
         sys.exit(1)
@@ -342,6 +368,7 @@ def run_allgather(args, w, torch, cpa, synth) -> dict:
               "parallelism": "one AllGather-KV rank's share on one GPU"}
     res = result_line(args, useful_flops, ms_step, ph["attn"], config,
                       traffic_for(KERNEL_SRC, w.name, rank))
+    res["attn_ms_median"] = round(float(sorted(per["attn"])[len(per["attn"]) // 2]), 4)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_allgather(w, h_q, q_loc, k_g, v_g, doc_cu, q_start,
                                                      args.cpu_rows, packed)
