@@ -108,6 +108,16 @@ def oracle_threads() -> int:
         return os.cpu_count() or 1
 
 
+def oracle_blas() -> str:
+    """BLAS library behind the oracle's numpy (name and version)."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        return " ".join(filter(None, [blas[0].get("internal_api"), blas[0].get("version")])) if blas else "unknown"
+    except Exception:
+        return "unknown"
+
+
 def cpu_baseline(w, meta_lists, q_loc, k_seq, v_seq, n_rows: int):
     """Time the fp64 oracle on an evenly spaced sample of query rows of the
     same rank share; scale to useful TFLOP/s."""
@@ -129,6 +139,7 @@ def cpu_baseline(w, meta_lists, q_loc, k_seq, v_seq, n_rows: int):
         flops += 4 * w.d * w.h_q * int(np.sum(loc + off + 1))
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "blas": oracle_blas(),
             "sample": f"{per * len(segs)} query rows ({per} evenly spaced per zigzag half) x {w.h_q} heads "
                       f"of the same rank share, all visible keys, numpy float64; {dt:.1f} s"}
 
@@ -183,6 +194,7 @@ def cpu_baseline_allgather(w, h_q, q_loc, k_g, v_g, doc_cu, q_start, n_rows: int
                 visible += doc_cu[b + 1] - doc_cu[b]
     flops = 4 * w.d * h_q * visible
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "blas": oracle_blas(),
             "sample": f"{len(rows)} evenly spaced local query rows x {h_q} heads of the same share, "
                       f"all visible keys, numpy float64; {dt:.1f} s"}
 
