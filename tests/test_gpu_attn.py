@@ -344,3 +344,22 @@ def test_random_packed_allgather_sweep(seed):
         gc.assert_close(out, ref, f"packed sweep {seed} rank {r}")
         pad0 = max(0, cu[-1] - r * share)
         assert torch.all(out[pad0:] == 0)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_midsize_sweep_sampled(seed):
+    """Seeded mid-size causal shares (2k-12k tokens per sequence, so the
+    unmasked key loop runs many unrolled iterations) in every page mode;
+    sampled rows of every rank, including each work item's first and last."""
+    rng = np.random.default_rng(4000 + seed)
+    cp = int(rng.choice([2, 4, 8]))
+    bs = int(rng.integers(1, 3))
+    lens = [int(rng.integers(2048, 12289)) for _ in range(bs)]
+    prefix = [int(rng.integers(0, 3000)) if rng.random() < 0.3 else 0 for _ in range(bs)]
+    h_kv = int(rng.choice([1, 2, 4]))
+    h_q = h_kv * int(rng.choice([1, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    ps = int(rng.choice([4, 16, 32, 64, 256]))
+    print("midsize", seed, "cp", cp, "lens", lens, "prefix", prefix, "heads", h_q, h_kv, "d", d, "ps", ps,
+          flush=True)
+    _prefix_extend_case(cp, lens, prefix, h_q, h_kv, d, ps, 6000 + seed, sample=6)
