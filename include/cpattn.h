@@ -208,8 +208,11 @@ int cp_zigzag_rerange(const void* d_blob, const cp_meta_t* meta, int32_t directi
  *   is written.  The page table's contents are the caller's contract (enough
  *   pages per sequence); they are not read on the host.  A token whose page
  *   id falls outside [0, num_pages) is skipped (never written out of bounds).
- * Errors: meta kind not zigzag, H_kv*D*2 not a multiple of 16, page_size < 1,
- * NULL/misaligned pointers -> CP_ERR_INVALID_ARG; launch failure -> CP_ERR_HIP.
+ * Errors: NULL meta or d_blob, meta kind not zigzag (or another version),
+ * H_kv < 1, D < 1, page_size < 1, num_pages < 1, NULL or misaligned pointers
+ * -> CP_ERR_INVALID_ARG; H_kv*D*2 not a multiple of 16 -> CP_ERR_UNSUPPORTED;
+ * rows of more than 2^27 16-byte vectors or a grid past 2^31 workgroups ->
+ * CP_ERR_OVERFLOW; launch failure -> CP_ERR_HIP.
  */
 int cp_kv_scatter(const void* d_blob, const cp_meta_t* meta,
                   const void* k_gathered, const void* v_gathered,
