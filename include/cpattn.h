@@ -188,8 +188,9 @@ int cp_allgather_packed_meta_build(int32_t n_docs, const int32_t* doc_cu, int32_
  *   narrow per-token tensors) in elements of the widest power of two up to
  *   8 bytes that divides row_bytes.  src and dst must be 16-byte aligned and
  *   must not overlap.
- * Errors: bad direction, meta kind not zigzag, row_bytes <= 0, NULL or
- * misaligned pointers -> CP_ERR_INVALID_ARG; launch failure -> CP_ERR_HIP.
+ * Errors: NULL meta or d_blob, meta kind not zigzag (or another version), bad
+ * direction, row_bytes <= 0, NULL or misaligned pointers -> CP_ERR_INVALID_ARG;
+ * a grid past 2^31 workgroups -> CP_ERR_OVERFLOW; launch failure -> CP_ERR_HIP.
  */
 int cp_zigzag_rerange(const void* d_blob, const cp_meta_t* meta, int32_t direction,
                       const void* src, void* dst, int64_t row_bytes, hipStream_t stream);
@@ -243,10 +244,13 @@ int cp_kv_scatter(const void* d_blob, const cp_meta_t* meta,
  *     (whole pages per key tile when it is >= page_size); a meta whose
  *     kv_align overstates the segments' alignment gives unspecified results,
  *     again with no out-of-bounds read.  The meta builders set it exactly.
- * Requires H_q % H_kv == 0 (else CP_ERR_INVALID_ARG, [P4]), H_q/H_kv equal to
- * meta->attn_group, D in {64, 128}, H_kv*D*2*64 < 2^31 (one 64-key tile of
- * all KV heads; else CP_ERR_UNSUPPORTED), page_size a power of two, scale
- * finite and > 0.
+ * Errors: NULL meta or d_blob, unknown meta kind or version, H_q % H_kv != 0
+ * ([P4]), H_q/H_kv different from meta->attn_group (the work list's), scale
+ * not finite or <= 0, num_pages < 1, NULL or misaligned (16-byte) pointers
+ * -> CP_ERR_INVALID_ARG; D not in {64, 128}, H_kv*D*2*64 >= 2^31 (one 64-key
+ * tile of all KV heads), page_size not a power of two up to 2^20 ->
+ * CP_ERR_UNSUPPORTED; a grid past 2^31 workgroups -> CP_ERR_OVERFLOW; launch
+ * failure -> CP_ERR_HIP.
  */
 int cp_prefill_attn(const void* q, const void* k_pool, const void* v_pool, void* out,
                     int32_t H_q, int32_t H_kv, int32_t D, float scale,
