@@ -306,3 +306,19 @@ def test_default_scale_values():
     assert oatt.default_scale(16) == 0.25
     assert oatt.default_scale(256) == 0.0625
     assert abs(oatt.default_scale(128) ** 2 * 128 - 1.0) < 1e-15
+
+
+def test_softmax_closed_form_at_large_scores():
+    """Two keys whose scores are about 800 and differ by ln 3: the weights are
+    exactly 1/4 and 3/4 (softmax depends on score differences only), so
+    O = (v0 + 3 v1) / 4.  exp(800) overflows float64, so the row maximum
+    must be subtracted before exponentiating."""
+    d = 4
+    q = np.zeros((1, 1, d))
+    q[0, 0, 0] = 1.0
+    k = np.zeros((2, 1, d))
+    k[0, 0, 0] = 800.0
+    k[1, 0, 0] = 800.0 + math.log(3.0)
+    v = np.array([[[1.0, 0.0, 2.0, -4.0]], [[5.0, 4.0, -2.0, 0.0]]])
+    out = oatt.attention(q, k, v, causal=False, scale=1.0)
+    np.testing.assert_allclose(out[0, 0], (v[0, 0] + 3 * v[1, 0]) / 4, rtol=0, atol=1e-12)
