@@ -3,7 +3,9 @@
 Each case plants one mistake (an off-by-one mask, the other alignment, an
 interleaved head mapping, a missing max subtraction, a wrong scale, a
 document boundary slip, a misplaced block remainder, an ignored reverse
-index, a scatter off by one token) in a temporary copy of ``oracle/`` and
+index, a scatter off by one token, and slips in the zigzag metadata: kv
+lengths, the local row order, surplus and prefix handling, the late block)
+in a temporary copy of ``oracle/`` and
 runs the oracle's pin tests against that copy: every mutation must make them
 fail.  Nothing in the repository is modified."""
 
@@ -34,6 +36,22 @@ MUTATIONS = [
     ("oracle/zigzag_meta.py", "return [base + (1 if j < rem else 0) for j in range(nblocks)]",
      "return [base + (1 if j >= nblocks - rem else 0) for j in range(nblocks)]",
      "block remainder on the last blocks"),
+    ("oracle/zigzag_meta.py", "kv_len_next = [prefix[b] + sum(blk[b][: late(cp_rank) + 1]) for b in range(bs)]",
+     "kv_len_next = [prefix[b] + sum(blk[b][: late(cp_rank)]) for b in range(bs)]",
+     "kv_len_next without its own block"),
+    ("oracle/zigzag_meta.py", "kv_len_prev = [prefix[b] + sum(blk[b][: early(cp_rank) + 1]) for b in range(bs)]",
+     "kv_len_prev = [sum(blk[b][: early(cp_rank) + 1]) for b in range(bs)]",
+     "kv_len_prev without the cached prefix"),
+    ("oracle/zigzag_meta.py", """        return ([b * nblk + early(rk) for b in range(bs)] +
+                [b * nblk + late(rk) for b in range(bs)])""",
+     """        return [c for b in range(bs) for c in (b * nblk + early(rk), b * nblk + late(rk))]""",
+     "local rows interleaved per sequence"),
+    ("oracle/zigzag_meta.py", "        ext[-1] += surplus", "        ext[0] += surplus",
+     "surplus tokens to the first sequence"),
+    ("oracle/zigzag_meta.py", "prefix = [max(seqs[b] - ext[b], 0) for b in range(bs)]",
+     "prefix = [max(seqs[b], 0) for b in range(bs)]", "prefix taken as the full length"),
+    ("oracle/zigzag_meta.py", "        return nblk - 1 - rk", "        return (nblk - 1 - rk + 1) % nblk",
+     "late block index shifted"),
     ("oracle/layout.py", "return np.concatenate([chunks[i] for i in meta.cp_reverse_index], axis=0)",
      "return np.concatenate([chunks[i] for i in sorted(meta.cp_reverse_index)], axis=0)",
      "rerange ignores the reverse index"),
