@@ -19,7 +19,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "CpError", "Meta", "meta_build", "allgather_meta_build", "zigzag_rerange",
+    "CpError", "Meta", "meta_build", "allgather_meta_build", "allgather_packed_meta_build", "zigzag_rerange",
     "kv_scatter", "prefill_attn", "load_library", "LIB_PATH",
     "GATHERED_TO_ORIG", "ORIG_TO_GATHERED",
 ]

@@ -316,3 +316,30 @@ def test_binding_refuses_cpu_tensors():
         cpa.prefill_attn(q, torch.zeros(4, 16, 2, 64, dtype=torch.bfloat16),
                          torch.zeros(4, 16, 2, 64, dtype=torch.bfloat16), q.clone(), m, 0.125, 16,
                          torch.zeros(2, dtype=torch.int32), torch.zeros(4, dtype=torch.int32))
+
+
+def test_ctypes_meta_mirror_matches_the_c_layout(tmp_path):
+    """The binding's CMeta must have cp_meta_t's size and field offsets, as the
+    C compiler lays the struct out (a mismatch would corrupt every call)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    names = [f[0] for f in cpa.CMeta._fields_]
+    prog = tmp_path / "layout.c"
+    prog.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "cpattn.h"\nint main(void) {\n'
+        '  printf("sizeof %zu\\n", sizeof(cp_meta_t));\n'
+        + "".join(f'  printf("{n} %zu\\n", offsetof(cp_meta_t, {n}));\n' for n in names)
+        + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    build = subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(root, "include"),
+                            "-I", "/opt/rocm/include", str(prog), "-o", str(exe)],
+                           capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    out = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.splitlines())
+    assert int(out["sizeof"]) == ctypes.sizeof(cpa.CMeta)
+    for n in names:
+        assert int(out[n]) == getattr(cpa.CMeta, n).offset, n
