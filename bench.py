@@ -31,6 +31,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -60,6 +62,11 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=768, help="query rows in the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip timing attention on the other workload shapes")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/traffic.json from rocprofv3 --pmc runs of FETCH_SIZE and WRITE_SIZE "
+                         "(bench step, then --calibrate-copy) and exit")
     return ap.parse_args()
 
 
@@ -77,7 +84,7 @@ def calibrate_copy(steps: int) -> None:
 
 
 def kernel_sha256(paths) -> str:
-    """SHA-256 over the attention kernel's device sources, in order."""
+    """SHA-256 over a kernel's device sources, in order."""
     h = hashlib.sha256()
     for p in paths:
         with open(p, "rb") as f:
@@ -85,18 +92,71 @@ def kernel_sha256(paths) -> str:
     return h.hexdigest()
 
 
-def traffic_for(kernel_srcs, workload: str, rank: int):
-    """Measured HBM bytes per attention launch, if the committed counter
-    summary was taken on this exact kernel source, workload and rank."""
-    path = os.path.join(ROOT, "profiles", "attn_traffic.json")
-    if not os.path.exists(path):
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def traffic_for(kernel: str, workload: str, rank: int):
+    """Measured HBM bytes per launch of ``kernel`` (FETCH_SIZE and WRITE_SIZE
+    counters scaled by the plain-copy calibration), if the committed record
+    was taken on this exact kernel source, workload and rank; else None."""
+    if not os.path.exists(TRAFFIC_PATH):
         return None
-    with open(path) as f:
-        rec = json.load(f)
-    sha = kernel_sha256(kernel_srcs)
-    if rec.get("kernel_sha256") != sha or rec.get("workload") != workload or rec.get("rank") != rank:
+    with open(TRAFFIC_PATH) as f:
+        recs = json.load(f)
+    rec = recs.get("kernels", {}).get(kernel)
+    if rec is None or recs.get("workload") != workload or recs.get("rank") != rank:
+        return None
+    if rec.get("kernel_sha256") != kernel_sha256(KERNEL_SRC[kernel]):
         return None
     return rec.get("bytes_per_launch")
+
+
+def _counter_means(run_dir: str, counter: str):
+    """Mean counter value (KiB) per dispatch, by kernel, from a rocprofv3
+    --pmc run's counter_collection CSV under run_dir."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for fn in files:
+        with open(fn) as f:
+            for i, row in enumerate(csv.DictReader(f)):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row["Kernel_Name"]
+                key = next((k for k in KERNEL_SRC if k in name), "copy" if "copyBuffer" in name else None)
+                if key is None:
+                    continue
+                disp = (fn, row.get("Dispatch_Id") or i)
+                per.setdefault(key, {})
+                per[key][disp] = per[key].get(disp, 0.0) + float(row["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def record_traffic(fetch_dir, write_dir, fetch_copy_dir, write_copy_dir, workload, rank):
+    """Write profiles/traffic.json from four rocprofv3 --pmc runs: FETCH_SIZE
+    and WRITE_SIZE of the bench step, and of --calibrate-copy (1 GiB read +
+    1 GiB written per launch), which gives the scale of each counter."""
+    fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
+    cf, cw = _counter_means(fetch_copy_dir, "FETCH_SIZE")["copy"], _counter_means(write_copy_dir, "WRITE_SIZE")["copy"]
+    gib_kib = float(1 << 20)
+    ff, wf = gib_kib / cf, gib_kib / cw
+    out = {"workload": workload, "rank": rank,
+           "copy_calibration": {"bytes_read": 1 << 30, "bytes_written": 1 << 30, "fetch_size_kib": cf,
+                                "write_size_kib": cw, "fetch_factor": ff, "write_factor": wf},
+           "kernels": {}}
+    for k in KERNEL_SRC:
+        if k not in fetch or k not in write:
+            continue
+        out["kernels"][k] = {
+            "kernel_sha256": kernel_sha256(KERNEL_SRC[k]),
+            "fetch_size_kib_per_launch": fetch[k], "write_size_kib_per_launch": write[k],
+            "bytes_per_launch": int(round((fetch[k] * ff + write[k] * wf) * 1024))}
+    with open(TRAFFIC_PATH, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def oracle_threads() -> int:
@@ -210,11 +270,13 @@ def run_timed(torch, step, names, warmup: int, steps: int):
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
+    allocs0 = torch.cuda.memory_stats().get("allocation.all.allocated", 0)
     t0 = time.perf_counter()
     for k in range(steps):
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    run_timed.allocations = torch.cuda.memory_stats().get("allocation.all.allocated", 0) - allocs0
     per = {n: [ev[i].elapsed_time(ev[i + 1]) for ev in evs] for i, n in enumerate(names)}
     return wall * 1e3 / steps, {n: sum(v) / steps for n, v in per.items()}, per
 
@@ -246,9 +308,13 @@ def result_line(args, useful_flops: float, ms_step: float, attn_ms: float, confi
     }
 
 
-# the attention kernel's device code and the table layouts it reads
-KERNEL_SRC = [os.path.join(ROOT, "context_prefill_attention_amd", "csrc", f)
-              for f in ("cp_attn_kernel.h", "cp_internal.h")]
+# each kernel's device code and the table layouts it reads
+_CSRC = os.path.join(ROOT, "context_prefill_attention_amd", "csrc")
+KERNEL_SRC = {
+    "attn_kernel": [os.path.join(_CSRC, f) for f in ("cp_attn_kernel.h", "cp_internal.h")],
+    "rerange_kernel": [os.path.join(_CSRC, f) for f in ("cp_copy.hip", "cp_internal.h")],
+    "scatter_kernel": [os.path.join(_CSRC, f) for f in ("cp_copy.hip", "cp_internal.h")],
+}
 
 
 def run_zigzag(args, w, torch, cpa, synth) -> dict:
@@ -280,8 +346,10 @@ def run_zigzag(args, w, torch, cpa, synth) -> dict:
     rerange_bytes = 2 * 2 * total * row_bytes      # K and V, each read once and written once
     scatter_bytes = 2 * 2 * total * row_bytes
 
+    mbuf = cpa.MetaBuffers(dev)   # staging reused by every step: no allocation per build
+
     def step(ev):
-        meta = cpa.meta_build(w.cp_size, rank, lens, attn_group=group, device=dev)
+        meta = cpa.meta_build(w.cp_size, rank, lens, attn_group=group, buffers=mbuf)
         if ev:
             ev[0].record()
         cpa.kv_scatter(meta, k_gd, v_gd, k_pool, v_pool, w.page_size, ip, ix)
@@ -303,16 +371,21 @@ def run_zigzag(args, w, torch, cpa, synth) -> dict:
               "seq_len": total, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.d,
               "page_size": w.page_size, "parallelism": "one CP rank's share on one GPU"}
     res = result_line(args, useful_flops, ms_step, ph["attn"], config,
-                      traffic_for(KERNEL_SRC, w.name, rank))
+                      traffic_for("attn_kernel", w.name, rank))
     res["attn_ms_median"] = round(float(sorted(per["attn"])[len(per["attn"]) // 2]), 4)
+    res["torch_allocations_in_timed_steps"] = run_timed.allocations
     roofline = res.pop("roofline")
+    rer_t, sc_t = traffic_for("rerange_kernel", w.name, rank), traffic_for("scatter_kernel", w.name, rank)
     res.update({
         "rerange_kv_ms": round(ph["rerange"], 4),
         "rerange_gbps": round(rerange_bytes / (ph["rerange"] * 1e-3) / 1e9, 1),
         "rerange_frac_of_hbm_peak": round(rerange_bytes / (ph["rerange"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        # one rerange launch moves K or V: algorithmic bytes vs the counters
+        "rerange_bytes_per_launch": {"algorithmic": rerange_bytes // 2, "counters": rer_t},
         "scatter_kv_ms": round(ph["scatter"], 4),
         "scatter_gbps": round(scatter_bytes / (ph["scatter"] * 1e-3) / 1e9, 1),
         "scatter_frac_of_hbm_peak": round(scatter_bytes / (ph["scatter"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "scatter_bytes_per_launch": {"algorithmic": scatter_bytes, "counters": sc_t},
         "roofline": roofline,
     })
     if not args.no_cpu_baseline:
@@ -340,10 +413,10 @@ def run_allgather(args, w, torch, cpa, synth) -> dict:
     q_real = max(0, min(share, w.kv_real - q_start))
     group = h_q // h_kv
 
-    def build(device):
+    def build(buffers):
         if packed:
-            return cpa.allgather_packed_meta_build(doc_cu, q_start, share, group, device=device)
-        return cpa.allgather_meta_build(share, q_real, w.kv_real, group, device=device)
+            return cpa.allgather_packed_meta_build(doc_cu, q_start, share, group, buffers=buffers)
+        return cpa.allgather_meta_build(share, q_real, w.kv_real, group, buffers=buffers)
 
     qg, k_g, v_g = synth.normal_bf16(w.seed, (w.kv_total, h_q, w.d), (w.kv_total, h_kv, w.d),
                                      (w.kv_total, h_kv, w.d))
@@ -362,8 +435,10 @@ def run_allgather(args, w, torch, cpa, synth) -> dict:
                 (doc_cu[b + 1] - doc_cu[b]) for b in range(len(doc_cu) - 1))
     useful_flops = 4 * w.d * h_q * pairs
 
+    mbuf = cpa.MetaBuffers(dev)
+
     def step(ev):
-        meta = build(dev)
+        meta = build(mbuf)
         if ev:
             ev[0].record()
         cpa.prefill_attn(q_d, k_pool, v_pool, out, meta, scale, w.page_size, ip, ix)
@@ -379,16 +454,125 @@ def run_allgather(args, w, torch, cpa, synth) -> dict:
               "h_q": h_q, "h_kv": h_kv, "head_dim": w.d, "page_size": w.page_size,
               "parallelism": "one AllGather-KV rank's share on one GPU"}
     res = result_line(args, useful_flops, ms_step, ph["attn"], config,
-                      traffic_for(KERNEL_SRC, w.name, rank))
+                      traffic_for("attn_kernel", w.name, rank))
     res["attn_ms_median"] = round(float(sorted(per["attn"])[len(per["attn"]) // 2]), 4)
+    res["torch_allocations_in_timed_steps"] = run_timed.allocations
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_allgather(w, h_q, q_loc, k_g, v_g, doc_cu, q_start,
                                                      args.cpu_rows, packed)
     return res
 
 
+def time_launches(torch, launch, warmup: int, iters: int) -> float:
+    """Mean ms per launch over ``iters`` back-to-back launches (HIP events on
+    the current stream, after ``warmup`` untimed ones)."""
+    for _ in range(warmup):
+        launch()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        launch()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+# Attention on the other workload shapes: (workload, rank, H_kv override or
+# None, cached-prefix lengths or None).  The prefix share is the cached
+# prefix + extend case: cp 4, a 4096-token prefix ahead of an 8192-token
+# extend, next to a 6144-token sequence without prefix, pages of 64.
+OTHER_CONFIGS = (
+    [("tiny_cp2_s256", r, None) for r in (0, 1)]
+    + [("gqa_cp2_s8192", r, None) for r in (0, 1)]
+    + [("varlen_cp4_bs8", r, None) for r in range(4)]
+    + [("allgather_kv_s32768", 1, h) for h in (8, 1)]
+    + [("allgather_packed_s32768", r, 8) for r in (1, 3)]
+    + [("prefix_cp4_p4096_e8192", r, None) for r in range(4)]
+)
+PREFIX_SHARE = {"extend": [8192, 6144], "prefix": [4096, 0], "cp_size": 4, "h_q": 32, "h_kv": 4,
+                "d": 128, "page_size": 64, "seed": 41}
+
+
+def other_configs(torch, cpa, synth) -> list:
+    """Time cp_prefill_attn alone on every other workload shape.  Inputs are
+    seeded N(0,1) bf16 drawn on the device (their values do not change the
+    work); page tables and metadata are the workloads' own."""
+    dev = torch.device("cuda", 0)
+    out = []
+    for name, rank, hkv in OTHER_CONFIGS:
+        gen = torch.Generator(device=dev)
+        if name == "prefix_cp4_p4096_e8192":
+            ps_ = PREFIX_SHARE
+            cp, h_q, h_kv, d, ps = ps_["cp_size"], ps_["h_q"], ps_["h_kv"], ps_["d"], ps_["page_size"]
+            lens, prefix = ps_["extend"], ps_["prefix"]
+            full = [e + p for e, p in zip(lens, prefix)]
+            gen.manual_seed(ps_["seed"] * 100 + rank)
+            wp = synth.Workload(name=name, seed=ps_["seed"], causal=True, h_q=h_q, h_kv=h_kv, d=d,
+                                page_size=ps, contiguous_kv=False, cp_size=cp)
+            meta = cpa.meta_build(cp, rank, lens, seq_lens=full, attn_group=h_q // h_kv, device=dev)
+            indptr, indices, n_pages = synth.page_table(wp, full)
+            causal = True
+        else:
+            w = synth.WORKLOADS[name]
+            d, ps = w.d, w.page_size
+            h_q, h_kv = w.h_q, (hkv or w.h_kv)
+            gen.manual_seed(w.seed * 100 + rank)
+            causal = w.causal
+            if causal:
+                lens = synth.sequence_lengths(w)
+                meta = cpa.meta_build(w.cp_size, rank, lens, attn_group=h_q // h_kv, device=dev)
+                indptr, indices, n_pages = synth.page_table(w, lens)
+            else:
+                share = w.kv_total // w.ag_degree
+                q_start = rank * share
+                if w.packed_docs is not None:
+                    doc_cu = synth.packed_doc_cu(w)
+                    meta = cpa.allgather_packed_meta_build(doc_cu, q_start, share, h_q // h_kv, device=dev)
+                else:
+                    doc_cu = [0, w.kv_real]
+                    meta = cpa.allgather_meta_build(share, max(0, min(share, w.kv_real - q_start)), w.kv_real,
+                                                    h_q // h_kv, device=dev)
+                n_pages = w.kv_total // ps
+                indptr, indices = np.array([0, n_pages], np.int32), np.arange(n_pages, dtype=np.int32)
+        q = torch.randn(meta.n_local_rows, h_q, d, generator=gen, device=dev).to(torch.bfloat16)
+        kp = torch.randn(n_pages, ps, h_kv, d, generator=gen, device=dev).to(torch.bfloat16)
+        vp = torch.randn(n_pages, ps, h_kv, d, generator=gen, device=dev).to(torch.bfloat16)
+        if not causal:       # the pad suffix must never be read
+            kp.view(-1, h_kv, d)[w.kv_real:] = float("nan")
+            vp.view(-1, h_kv, d)[w.kv_real:] = float("nan")
+            pairs = sum(max(0, min(doc_cu[b + 1], q_start + share) - max(doc_cu[b], q_start)) *
+                        (doc_cu[b + 1] - doc_cu[b]) for b in range(len(doc_cu) - 1))
+        else:
+            pairs = sum(causal_pairs(qn, kv) for qn, kv in
+                        zip(meta.q_prev + meta.q_next, meta.kv_len_prev + meta.kv_len_next))
+        ip, ix = torch.from_numpy(indptr).to(dev), torch.from_numpy(indices).to(dev)
+        o = torch.empty_like(q)
+        scale = 1.0 / math.sqrt(d)
+        flops = 4 * d * h_q * pairs
+
+        def launch():
+            cpa.prefill_attn(q, kp, vp, o, meta, scale, ps, ip, ix)
+        est = time_launches(torch, launch, 3, 3)
+        iters = int(min(400, max(10, 60.0 / max(est, 1e-3))))
+        ms = time_launches(torch, launch, max(5, iters // 4), iters)
+        if not torch.isfinite(o).all():
+            print(f"non-finite attention output on {name} rank {rank}", file=sys.stderr)
+            sys.exit(1)
+        tf = flops / (ms * 1e-3) / 1e12
+        out.append({"workload": name, "rank": rank, "h_q": h_q, "h_kv": h_kv, "page_size": ps,
+                    "attn_ms": round(ms, 4), "useful_tflops": round(tf, 1),
+                    "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "launches_timed": iters})
+        del q, kp, vp, o
+    return out
+
+
 def main():
     args = parse()
+    if args.record_traffic:
+        import synth
+        w = synth.WORKLOADS[args.workload]
+        record_traffic(*args.record_traffic, w.name, w.ranks[0] if args.rank is None else args.rank)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the exchange between GPUs is not implemented (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -409,6 +593,8 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     res = run_zigzag(args, w, torch, cpa, synth) if w.causal else run_allgather(args, w, torch, cpa, synth)
+    if not args.no_other_configs and args.workload == "long_cp8_s131072_r3":
+        res["other_configs"] = other_configs(torch, cpa, synth)
     print(json.dumps(res), flush=True)
 
 

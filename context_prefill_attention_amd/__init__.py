@@ -19,7 +19,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = [
-    "CpError", "Meta", "meta_build", "allgather_meta_build", "allgather_packed_meta_build", "zigzag_rerange",
+    "CpError", "Meta", "MetaBuffers", "meta_build", "allgather_meta_build", "allgather_packed_meta_build", "zigzag_rerange",
     "kv_scatter", "prefill_attn", "load_library", "LIB_PATH",
     "GATHERED_TO_ORIG", "ORIG_TO_GATHERED",
 ]
@@ -149,8 +149,16 @@ class Meta:
             return getattr(c, name)
         raise AttributeError(name)
 
-    def to_device(self, device=None, non_blocking: bool = True):
-        """Copy the blob to device memory on the current stream (one H2D copy)."""
+    def to_device(self, device=None, non_blocking: bool = True, buffers: "Optional[MetaBuffers]" = None):
+        """Copy the blob to device memory on the current stream (one H2D copy).
+
+        Without ``buffers`` a pinned staging tensor and a device tensor are
+        allocated for this metadata.  With ``buffers`` (a ``MetaBuffers``
+        reused across calls) nothing is allocated once the buffers are large
+        enough: the device copy lives in ``buffers`` until its next upload."""
+        if buffers is not None:
+            self.d_blob = buffers.upload(self.blob)
+            return self
         import torch
         dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
         pinned = torch.empty(self.blob.size, dtype=torch.uint8, pin_memory=True)
@@ -162,10 +170,75 @@ class Meta:
         return self
 
 
+class MetaBuffers:
+    """Caller-owned staging for metadata blobs, reused call after call (the
+    preallocated page-pointer array of the "Zigzag cp #3" pull request,
+    instead of tensors built per call).
+
+    Holds two pinned host buffers, used in turn, and one device buffer.  An
+    upload waits (on the host) only until the copy that last read the pinned
+    buffer it is about to refill has finished, i.e. when the GPU is two
+    uploads behind; it then enqueues one asynchronous copy on the current
+    stream.  The device buffer is overwritten by the next upload, so one
+    ``MetaBuffers`` serves one live metadata at a time, and all its uploads
+    and the kernels reading them must go to one stream.  Buffers grow (the
+    only allocation) when a blob is larger than any before."""
+
+    def __init__(self, device=None, capacity: int = 1 << 16):
+        import torch
+        self._torch = torch
+        if device is None:
+            device = torch.device("cuda", torch.cuda.current_device())
+        self.device = torch.device(device)
+        self._pin = self.device.type == "cuda"
+        self.capacity = 0
+        self._host = [None, None]
+        self._events = [None, None]
+        self._dev = None
+        self._turn = 0
+        self.grow_count = 0
+        self._ensure(int(capacity))
+
+    def _ensure(self, nbytes: int) -> None:
+        if nbytes <= self.capacity:
+            return
+        torch = self._torch
+        cap = max(nbytes, 2 * self.capacity)
+        if self._pin:
+            torch.cuda.current_stream(self.device).synchronize()   # old buffers may still be read
+        self._host = [torch.empty(cap, dtype=torch.uint8, pin_memory=self._pin) for _ in range(2)]
+        self._events = [None, None]
+        self._dev = torch.empty(cap, dtype=torch.uint8, device=self.device)
+        self.capacity = cap
+        self.grow_count += 1
+
+    def upload(self, blob: np.ndarray):
+        """Stage ``blob`` and enqueue its copy to the device buffer; returns
+        the device view holding it."""
+        torch = self._torch
+        n = int(blob.size)
+        self._ensure(n)
+        i = self._turn
+        self._turn ^= 1
+        ev = self._events[i]
+        if ev is not None:
+            ev.synchronize()          # the copy that last read this staging buffer is done
+        host = self._host[i]
+        host.numpy()[:n] = blob
+        d = self._dev[:n]
+        d.copy_(host[:n], non_blocking=self._pin)
+        if self._pin:
+            if ev is None:
+                ev = self._events[i] = torch.cuda.Event()
+            ev.record()
+        return d
+
+
 def meta_build(cp_size: int, cp_rank: int, extend_lens: Sequence[int],
                seq_lens: Optional[Sequence[int]] = None, num_tokens: Optional[int] = None,
-               attn_group: int = 0, device=None) -> Meta:
-    """``cp_meta_build``: host-only zigzag metadata; ``device`` also copies it H2D."""
+               attn_group: int = 0, device=None, buffers: Optional[MetaBuffers] = None) -> Meta:
+    """``cp_meta_build``: host-only zigzag metadata; ``device`` (or reusable
+    ``buffers``) also copies it H2D."""
     lib = load_library()
     ext, ext_p = _i32_array(extend_lens)
     seq, seq_p = _i32_array(seq_lens)
@@ -179,11 +252,13 @@ def meta_build(cp_size: int, cp_rank: int, extend_lens: Sequence[int],
     _check(lib.cp_meta_build(cp_size, cp_rank, int(ext.size), ext_p, seq_p, n_tok, attn_group,
                              blob.ctypes.data, blob.size, ctypes.byref(cm)))
     m = Meta(cm, blob)
+    if buffers is not None:
+        return m.to_device(buffers=buffers)
     return m.to_device(device) if device is not None else m
 
 
 def allgather_meta_build(q_total: int, q_real: int, kv_len: int, attn_group: int,
-                         device=None) -> Meta:
+                         device=None, buffers: Optional[MetaBuffers] = None) -> Meta:
     """``cp_allgather_meta_build``: metadata of the non-causal AllGather-KV share."""
     lib = load_library()
     cm = CMeta()
@@ -192,11 +267,13 @@ def allgather_meta_build(q_total: int, q_real: int, kv_len: int, attn_group: int
     _check(lib.cp_allgather_meta_build(q_total, q_real, kv_len, attn_group, blob.ctypes.data,
                                        blob.size, ctypes.byref(cm)))
     m = Meta(cm, blob)
+    if buffers is not None:
+        return m.to_device(buffers=buffers)
     return m.to_device(device) if device is not None else m
 
 
 def allgather_packed_meta_build(doc_cu, q_start: int, q_total: int, attn_group: int,
-                                device=None) -> Meta:
+                                device=None, buffers: Optional[MetaBuffers] = None) -> Meta:
     """``cp_allgather_packed_meta_build``: metadata of the non-causal
     AllGather-KV share of a packed global sequence (document boundaries
     ``doc_cu``; local query rows are global rows [q_start, q_start+q_total))."""
@@ -212,6 +289,8 @@ def allgather_packed_meta_build(doc_cu, q_start: int, q_total: int, attn_group: 
     _check(lib.cp_allgather_packed_meta_build(cu.size - 1, cup, q_start, q_total, attn_group,
                                               blob.ctypes.data, blob.size, ctypes.byref(cm)))
     m = Meta(cm, blob)
+    if buffers is not None:
+        return m.to_device(buffers=buffers)
     return m.to_device(device) if device is not None else m
 
 

@@ -49,8 +49,11 @@ extern "C" int cp_prefill_attn(const void* q, const void* k_pool, const void* v_
     return set_error(CP_ERR_INVALID_ARG, "a device pointer is NULL");
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
     return set_error(CP_ERR_INVALID_ARG, "q, k_pool, v_pool and out must be 16-byte aligned");
+  // HIP rejects a launch whose grid holds more than 2^32-1 work-items.
   const int64_t grid = (int64_t)meta->n_work * H_kv;
-  if (grid > 2147483647LL) return set_error(CP_ERR_OVERFLOW, "attention grid too large");
+  if (grid > 4294967295LL / kThreads)
+    return set_error(CP_ERR_OVERFLOW, "attention grid too large (%lld workgroups of %d threads)",
+                     (long long)grid, kThreads);
   if (grid == 0) return CP_OK;
   AttnArgs args;
   args.q = static_cast<const unsigned char*>(q);

@@ -153,7 +153,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   constexpr bool PAGE_PER_TILE = PM == kPageTile;
   constexpr int GP = PM >= 16 ? PM : 0;                // page size of the group modes
   constexpr int NPP = GP ? kAttnKeys / GP : 1;         // pages per tile in the group modes
-  constexpr int PLOADS = PM == kPageLane ? LOADS : 0;  // vector page-id loads per lane per tile
   static_assert(LOADS >= 1 && TILE_BYTES % (kThreads * 16) == 0, "loader shape");
   // K and V rings of kStages tiles, one array per stage: the compiler can
   // then tell the stage being read from the stages whose direct loads are
@@ -251,26 +250,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   // lane's rows.
   constexpr int NPG = PAGE_PER_TILE ? 2 : (GP != 0 ? NPP : LOADS);
   struct Pages { int p[NPG]; };
+  // Every page-table read stays inside the segment's row [0, n_entries): a
+  // row shorter than its keys need repeats its last entry (those keys then
+  // read a wrong page, never memory outside the table), and an empty row
+  // reads as page -1, which the loads redirect like any invalid page id.
+  const int last_entry = max(n_entries - 1, 0);
+  auto entry = [&](int e) -> int { return n_entries > 0 ? ptab[min(e, last_entry)] : -1; };
   auto fetch_pages = [&](int t) -> Pages {
     Pages pg;
     if constexpr (PAGE_PER_TILE) {
       const int e0 = (kv0 + min(t, n_tiles - 1) * kAttnKeys) >> shift;
-      pg.p[0] = ptab[e0];
-      pg.p[1] = straddle ? ptab[min(e0 + 1, n_entries - 1)] : pg.p[0];
+      pg.p[0] = entry(e0);
+      pg.p[1] = straddle ? entry(e0 + 1) : pg.p[0];
     } else if constexpr (GP != 0) {
       const int e0 = (kv0 + min(t, n_tiles - 1) * kAttnKeys) >> shift;
 #pragma unroll
-      for (int j = 0; j < NPP; ++j) pg.p[j] = ptab[min(e0 + j, n_entries - 1)];
+      for (int j = 0; j < NPP; ++j) pg.p[j] = entry(e0 + j);
     } else {
 #pragma unroll
       for (int u = 0; u < LOADS; ++u) {
         const int key = max(0, min(t * kAttnKeys + ld_row[u], s.kv_len - 1));
-        pg.p[u] = ptab[(kv0 + key) >> shift];
+        pg.p[u] = entry((kv0 + key) >> shift);
       }
     }
     return pg;
   };
-  const int page0 = ptab[0];
+  const int page0 = entry(0);
   const bool page0_ok = page0 >= 0 && page0 < a.num_pages;
   // Per-lane part of a load address when a whole tile lies in one page.
   uint32_t ld_const[LOADS];
@@ -285,13 +290,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     const int first = kv0 + t * kAttnKeys;   // page-table position of the tile's key 0
     if (PAGE_PER_TILE && (t + 1) * kAttnKeys <= s.kv_len && pg.p[0] >= 0 && pg.p[0] < a.num_pages &&
         (first & ps_mask) + kAttnKeys <= ps_mask + 1) {
+      // wave-uniform tile base (scalar registers) plus a 32-bit per-lane
+      // offset: the loads take the scalar-base address form, no vector adds
       const uint64_t base =
           (((uint64_t)pg.p[0] << shift) | (uint32_t)(first & ps_mask)) * tok_stride;
+      const unsigned char* k_base = a.k_pool + base;
+      const unsigned char* v_base = a.v_pool + base;
 #pragma unroll
       for (int u = 0; u < LOADS; ++u) {
-        __builtin_amdgcn_global_load_lds(a.k_pool + (int64_t)(base + ld_const[u]),
+        __builtin_amdgcn_global_load_lds(k_base + (int64_t)ld_const[u],
             (__attribute__((address_space(3))) void*)&kd[(u * kWaves + wave) * 1024], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(a.v_pool + (int64_t)(base + ld_const[u]),
+        __builtin_amdgcn_global_load_lds(v_base + (int64_t)ld_const[u],
             (__attribute__((address_space(3))) void*)&vd[(u * kWaves + wave) * 1024], 16, 0, 0);
       }
       return;
@@ -330,11 +339,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     }
   };
   // Wait until tile t's direct loads have landed, given what this wave
-  // issued after them: the page ids of tile t+2 (with small pages) and the
-  // loads of tile t+1, if those tiles exist.
+  // issued after them: the loads of tile t+1, if it exists.  With small
+  // pages the page ids fetched in this step are vector loads too; the
+  // compiler may place them before or after the loads of tile t+1, so none
+  // of them is counted as allowed to stay outstanding.
   auto wait_tile = [&](int t) {
-    if (PLOADS != 0 && t + 2 < n_pad) wait_vmcnt<PLOADS + 2 * LOADS>();
-    else if (t + 1 < n_pad) wait_vmcnt<2 * LOADS>();
+    if (t + 1 < n_pad) wait_vmcnt<2 * LOADS>();
     else wait_vmcnt<0>();
   };
 
@@ -428,8 +438,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[j], c, -mc));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[j + 1], c, -mc));
       pb[j >> 1] = pack_bf16x2(p0, p1);
-      r0 += p0;
-      r1 += p1;
+      r0 = j ? r0 + p0 : p0;
+      r1 = j ? r1 + p1 : p1;
     }
     return r0 + r1;
   };
@@ -450,8 +460,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[j], c, -mc));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[j + 1], c, -mc));
       pb[j >> 1] = pack_bf16x2(p0, p1);
-      r0 += p0;
-      r1 += p1;
+      r0 = j ? r0 + p0 : p0;
+      r1 = j ? r1 + p1 : p1;
     }
     float rs = r0 + r1;
     if (__builtin_amdgcn_ballot_w64(!(rs <= kSumLimit)) != 0) {   // rare: raise the references

@@ -5,14 +5,16 @@
 // original token order (sglang zigzag.py source page: gather_kv_cache splits
 // the gathered rows by reverse_split_len and reorders them by
 // cp_reverse_index; _all_gather_reorganized pads every rank to max_rank_len).
-// The rerange is therefore one contiguous memcpy per chunk and the scatter
-// one row copy per token into its KV-pool slot (materialize_full_kv writes
-// the full-sequence K/V at the extend tokens' cache locations).
+// The rerange is therefore one contiguous memcpy per chunk, and the scatter
+// one contiguous copy per (chunk, pool page) run into that page's slots
+// (materialize_full_kv writes the full-sequence K/V at the extend tokens'
+// cache locations).
 //
 // Launch shape: a 1-D grid; each workgroup owns one fixed-size byte range
-// (rerange) or row block (scatter) of one chunk, so the chunk lookup is one
-// division and no search.  Each lane moves 16-byte vectors with several loads
-// in flight before the stores, which is what keeps HBM3E busy.
+// (16 KiB) of one chunk (rerange) or of one page run of a chunk (scatter), so
+// its lookups are a few divisions and no search.  Each lane moves 16-byte
+// vectors with several loads in flight before the stores, which is what
+// keeps HBM3E busy.
 #include <hip/hip_runtime.h>
 
 #include "../../include/cpattn.h"
@@ -76,69 +78,64 @@ __global__ __launch_bounds__(kCopyThreads) void rerange_narrow_kernel(
   for (int64_t i = threadIdx.x; i < n; i += kCopyThreads) d[i] = s[i];
 }
 
-constexpr int kScatterRows = 16;   // token rows per workgroup
-constexpr int kScatterUnroll = 4;  // 16-B vectors of K and of V per lane in flight
-
-// One workgroup copies rows [part*16, part*16+16) of chunk c, for K and V.
-// The destination row of every token is looked up once, into LDS.  Vector i
-// of the block (i = lane + k*threads) is row i / vpr, column i % vpr; each
-// lane steps its (row, column) pair by the thread count without dividing.
+// Scatter.  Within one chunk, the tokens that share a pool page are a
+// contiguous run of rows on both sides: consecutive rows of the gathered
+// buffer and consecutive slots of that page.  The grid is laid out as
+// (chunk, j-th page the chunk touches, 16 KiB slice of that run), so a
+// workgroup copies one contiguous byte range of K and of V, with a single
+// page-table lookup, exactly like the rerange.  Workgroups whose slice lies
+// past the end of their run exit at once.
 __global__ __launch_bounds__(kCopyThreads) void scatter_kernel(
-    const Chunk* __restrict__ chunks, int32_t parts_per_chunk,
+    const Chunk* __restrict__ chunks, int32_t pages_per_chunk, int32_t slices_per_page,
     const unsigned char* __restrict__ kg, const unsigned char* __restrict__ vg,
     unsigned char* __restrict__ kp, unsigned char* __restrict__ vp, int64_t row_bytes,
     int32_t num_pages, int32_t page_size, const int32_t* __restrict__ indptr,
     const int32_t* __restrict__ indices) {
-  __shared__ int64_t dst_row[kScatterRows];
-  const int c = blockIdx.x / parts_per_chunk;
-  const int part = blockIdx.x - c * parts_per_chunk;
+  const int per_chunk = pages_per_chunk * slices_per_page;
+  const int c = blockIdx.x / per_chunk;
+  const int rem = blockIdx.x - c * per_chunk;
+  const int j = rem / slices_per_page;
+  const int slice = rem - j * slices_per_page;
   const Chunk ch = chunks[c];
-  const int r0 = part * kScatterRows;
-  if (r0 >= ch.n_rows) return;
-  const int nrows = min(kScatterRows, ch.n_rows - r0);
-  if (threadIdx.x < nrows) {
-    const int pos = ch.pos0 + r0 + threadIdx.x;
-    const int page = indices[indptr[ch.b] + pos / page_size];
-    // a page id outside the pool is skipped rather than written out of bounds
-    dst_row[threadIdx.x] = (page >= 0 && page < num_pages) ? (int64_t)page * page_size + pos % page_size : -1;
-  }
-  __syncthreads();
-  const int vpr = (int)(row_bytes / 16);   // the host keeps kScatterRows * vpr within int32
-  const int total = vpr * nrows;
-  const int dr = kCopyThreads / vpr, dc = kCopyThreads - dr * vpr;
-  int r = (int)threadIdx.x / vpr;
-  int col = (int)threadIdx.x - r * vpr;
-  const unsigned char* ks = kg + ((int64_t)ch.g_row + r0) * row_bytes;
-  const unsigned char* vs = vg + ((int64_t)ch.g_row + r0) * row_bytes;
-  for (int i0 = 0; i0 < total; i0 += kCopyThreads * kScatterUnroll) {
-    u32x4 a[kScatterUnroll], b[kScatterUnroll];
-    int rr[kScatterUnroll], cc[kScatterUnroll];
+  // the run: positions [lo, hi) of page-table entry e = pos0/ps + j
+  const int e = ch.pos0 / page_size + j;
+  const int64_t page_first = (int64_t)e * page_size;
+  const int64_t lo = max((int64_t)ch.pos0, page_first);
+  const int64_t hi = min((int64_t)ch.pos0 + ch.n_rows, page_first + page_size);
+  if (lo >= hi) return;
+  const int64_t nbytes = (int64_t)(hi - lo) * row_bytes;
+  const int64_t start = (int64_t)slice * kCopyBytesPerWG;
+  if (start >= nbytes) return;
+  // the page id: an entry outside the sequence's row of the table, or an id
+  // outside the pool, leaves its slots untouched (nothing is written)
+  const int row0 = indptr[ch.b];
+  if (e >= indptr[ch.b + 1] - row0) return;
+  const int page = indices[row0 + e];
+  if (page < 0 || page >= num_pages) return;
+  const int64_t src_off = ((int64_t)ch.g_row + (lo - ch.pos0)) * row_bytes + start;
+  const int64_t dst_off = ((int64_t)page * page_size + (lo - page_first)) * row_bytes + start;
+  const int64_t avail = nbytes - start;
+  u32x4 a[kCopyUnroll], b[kCopyUnroll];
 #pragma unroll
-    for (int u = 0; u < kScatterUnroll; ++u) {
-      rr[u] = r;
-      cc[u] = col;
-      if (i0 + u * kCopyThreads + (int)threadIdx.x < total) {
-        const int64_t so = (int64_t)r * row_bytes + col * 16;
-        a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ks + so));
-        b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs + so));
-      }
-      r += dr;
-      col += dc;
-      if (col >= vpr) {
-        col -= vpr;
-        ++r;
-      }
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t off = (int64_t)(u * kCopyThreads + threadIdx.x) * 16;
+    if (off < avail) {
+      a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kg + src_off + off));
+      b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + src_off + off));
     }
+  }
 #pragma unroll
-    for (int u = 0; u < kScatterUnroll; ++u) {
-      if (i0 + u * kCopyThreads + (int)threadIdx.x < total && dst_row[rr[u]] >= 0) {
-        const int64_t dof = dst_row[rr[u]] * row_bytes + cc[u] * 16;
-        __builtin_nontemporal_store(a[u], reinterpret_cast<u32x4*>(kp + dof));
-        __builtin_nontemporal_store(b[u], reinterpret_cast<u32x4*>(vp + dof));
-      }
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t off = (int64_t)(u * kCopyThreads + threadIdx.x) * 16;
+    if (off < avail) {
+      __builtin_nontemporal_store(a[u], reinterpret_cast<u32x4*>(kp + dst_off + off));
+      __builtin_nontemporal_store(b[u], reinterpret_cast<u32x4*>(vp + dst_off + off));
     }
   }
 }
+
+// HIP rejects a launch whose grid holds more than 2^32-1 work-items.
+constexpr int64_t kMaxCopyGrid = 4294967295LL / kCopyThreads;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -162,8 +159,9 @@ extern "C" int cp_zigzag_rerange(const void* d_blob, const cp_meta_t* meta, int3
   const int64_t chunk_bytes = (int64_t)meta->max_chunk_rows * row_bytes;
   const int64_t parts = (chunk_bytes + kCopyBytesPerWG - 1) / kCopyBytesPerWG;
   const int64_t grid = parts * meta->n_chunks;
-  if (parts > 2147483647LL || grid > 2147483647LL)
-    return set_error(CP_ERR_OVERFLOW, "rerange grid too large");
+  if (parts > 2147483647LL || grid > kMaxCopyGrid)
+    return set_error(CP_ERR_OVERFLOW, "rerange grid too large (%lld workgroups of %d threads)",
+                     (long long)grid, kCopyThreads);
   if (grid == 0) return CP_OK;
   const Chunk* chunks = reinterpret_cast<const Chunk*>(static_cast<const char*>(d_blob) + meta->off_chunks);
   const int32_t fwd = direction == CP_RERANGE_GATHERED_TO_ORIG;
@@ -199,21 +197,27 @@ extern "C" int cp_kv_scatter(const void* d_blob, const cp_meta_t* meta,
   const int64_t row_bytes = (int64_t)H_kv * D * 2;
   if (row_bytes % 16 != 0)
     return set_error(CP_ERR_UNSUPPORTED, "H_kv*D*2=%lld must be a multiple of 16", (long long)row_bytes);
-  if (row_bytes / 16 * kScatterRows > 2147483647LL)
-    return set_error(CP_ERR_OVERFLOW, "H_kv*D*2=%lld is too large a row", (long long)row_bytes);
   if (page_size < 1) return set_error(CP_ERR_INVALID_ARG, "page_size=%d", page_size);
   if (num_pages < 1) return set_error(CP_ERR_INVALID_ARG, "num_pages=%d", num_pages);
   if (!k_gathered || !v_gathered || !k_pool || !v_pool || !kv_page_indptr || !kv_page_indices)
     return set_error(CP_ERR_INVALID_ARG, "a device pointer is NULL");
   if (!aligned16(k_gathered) || !aligned16(v_gathered) || !aligned16(k_pool) || !aligned16(v_pool))
     return set_error(CP_ERR_INVALID_ARG, "K/V buffers must be 16-byte aligned");
-  const int64_t parts = (meta->max_chunk_rows + kScatterRows - 1) / kScatterRows;
-  const int64_t grid = parts * meta->n_chunks;
-  if (grid > 2147483647LL) return set_error(CP_ERR_OVERFLOW, "scatter grid too large");
+  // A chunk of n rows touches at most ceil((n - 1) / ps) + 1 pages; a page's
+  // run is at most ps rows, i.e. ceil(ps * row_bytes / 16 KiB) slices.
+  const int64_t pages_per_chunk =
+      meta->max_chunk_rows > 0 ? (meta->max_chunk_rows - 1 + page_size - 1) / page_size + 1 : 0;
+  const int64_t slices_per_page = ((int64_t)page_size * row_bytes + kCopyBytesPerWG - 1) / kCopyBytesPerWG;
+  const int64_t grid = pages_per_chunk * slices_per_page * meta->n_chunks;
+  if (pages_per_chunk > 2147483647LL || slices_per_page > 2147483647LL ||
+      pages_per_chunk * slices_per_page > 2147483647LL || grid > kMaxCopyGrid)
+    return set_error(CP_ERR_OVERFLOW, "scatter grid too large (%lld workgroups of %d threads)",
+                     (long long)grid, kCopyThreads);
   if (grid == 0) return CP_OK;
   const Chunk* chunks = reinterpret_cast<const Chunk*>(static_cast<const char*>(d_blob) + meta->off_chunks);
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)grid), dim3(kCopyThreads), 0, stream, chunks,
-                     (int32_t)parts, static_cast<const unsigned char*>(k_gathered),
+                     (int32_t)pages_per_chunk, (int32_t)slices_per_page,
+                     static_cast<const unsigned char*>(k_gathered),
                      static_cast<const unsigned char*>(v_gathered), static_cast<unsigned char*>(k_pool),
                      static_cast<unsigned char*>(v_pool), row_bytes, num_pages, page_size,
                      kv_page_indptr, kv_page_indices);

@@ -190,7 +190,8 @@ int cp_allgather_packed_meta_build(int32_t n_docs, const int32_t* doc_cu, int32_
  *   must not overlap.
  * Errors: NULL meta or d_blob, meta kind not zigzag (or another version), bad
  * direction, row_bytes <= 0, NULL or misaligned pointers -> CP_ERR_INVALID_ARG;
- * a grid past 2^31 workgroups -> CP_ERR_OVERFLOW; launch failure -> CP_ERR_HIP.
+ * a grid of more than 2^24-1 workgroups (16 KiB each: HIP's 2^32-1 work-item
+ * limit at 256 threads) -> CP_ERR_OVERFLOW; launch failure -> CP_ERR_HIP.
  */
 int cp_zigzag_rerange(const void* d_blob, const cp_meta_t* meta, int32_t direction,
                       const void* src, void* dst, int64_t row_bytes, hipStream_t stream);
@@ -206,14 +207,19 @@ int cp_zigzag_rerange(const void* d_blob, const cp_meta_t* meta, int32_t directi
  *     page j of sequence b is kv_page_indices[kv_page_indptr[b] + j].
  *   Extend token t of sequence b goes to sequence position prefix_b + t, i.e.
  *   page (prefix_b+t)/page_size, slot (prefix_b+t)%page_size.  No other slot
- *   is written.  The page table's contents are the caller's contract (enough
- *   pages per sequence); they are not read on the host.  A token whose page
- *   id falls outside [0, num_pages) is skipped (never written out of bounds).
+ *   is written.  The page table is read only on the device, and only inside
+ *   each sequence's row: entry j of sequence b is read only when
+ *   j < kv_page_indptr[b+1] - kv_page_indptr[b].  A token whose entry lies
+ *   past its row, or whose page id falls outside [0, num_pages), is skipped
+ *   (its slot is not written; nothing is written out of bounds).  The CSR
+ *   itself (indptr non-decreasing, kv_page_indices holding indptr[bs]
+ *   entries) is the caller's contract.
  * Errors: NULL meta or d_blob, meta kind not zigzag (or another version),
  * H_kv < 1, D < 1, page_size < 1, num_pages < 1, NULL or misaligned pointers
  * -> CP_ERR_INVALID_ARG; H_kv*D*2 not a multiple of 16 -> CP_ERR_UNSUPPORTED;
- * rows of more than 2^27 16-byte vectors or a grid past 2^31 workgroups ->
- * CP_ERR_OVERFLOW; launch failure -> CP_ERR_HIP.
+ * a grid of more than 2^24-1 workgroups (one per 16 KiB of a page run of a
+ * chunk: HIP's 2^32-1 work-item limit at 256 threads) -> CP_ERR_OVERFLOW;
+ * launch failure -> CP_ERR_HIP.
  */
 int cp_kv_scatter(const void* d_blob, const cp_meta_t* meta,
                   const void* k_gathered, const void* v_gathered,
@@ -236,10 +242,13 @@ int cp_kv_scatter(const void* d_blob, const cp_meta_t* meta,
  *     sequences, then next halves).  Fp32 accumulation, bf16 output (RNE).
  *   k_pool, v_pool, num_pages, page table: as in cp_kv_scatter.  A
  *     contiguous [S, H_kv, D] tensor is the pool with page_size dividing S
- *     and the identity page table.  A key whose page id lies outside
- *     [0, num_pages) is read from the first slot of the segment's page-table
- *     row instead: no out-of-bounds read, but such a table gives unspecified
- *     results.
+ *     and the identity page table.  Page-table reads stay inside the
+ *     segment's row: a row with fewer than ceil(keys / page_size) entries
+ *     repeats its last entry for the missing ones, and an empty row reads as
+ *     an invalid page id.  A key whose page id lies outside [0, num_pages)
+ *     is read from the first slot of the segment's page-table row instead
+ *     (or slot 0 of the pool).  Neither case reads out of bounds, but such a
+ *     table gives unspecified results.
  *   meta->kv_align picks how page ids are fetched for pages under 64 keys
  *     (whole pages per key tile when it is >= page_size); a meta whose
  *     kv_align overstates the segments' alignment gives unspecified results,
@@ -249,8 +258,9 @@ int cp_kv_scatter(const void* d_blob, const cp_meta_t* meta,
  * not finite or <= 0, num_pages < 1, NULL or misaligned (16-byte) pointers
  * -> CP_ERR_INVALID_ARG; D not in {64, 128}, H_kv*D*2*64 >= 2^31 (one 64-key
  * tile of all KV heads), page_size not a power of two up to 2^20 ->
- * CP_ERR_UNSUPPORTED; a grid past 2^31 workgroups -> CP_ERR_OVERFLOW; launch
- * failure -> CP_ERR_HIP.
+ * CP_ERR_UNSUPPORTED; a grid (n_work * H_kv workgroups of 512 threads) of
+ * more than 2^23-1 workgroups (HIP's 2^32-1 work-item limit) ->
+ * CP_ERR_OVERFLOW; launch failure -> CP_ERR_HIP.
  */
 int cp_prefill_attn(const void* q, const void* k_pool, const void* v_pool, void* out,
                     int32_t H_q, int32_t H_kv, int32_t D, float scale,

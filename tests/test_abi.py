@@ -258,9 +258,18 @@ def test_allgather_meta_rejections(args, code):
 
 
 # Fake, never-dereferenced device addresses: every call below must fail on
-# the host before it could touch them.
+# the host before it could touch them.  A validation bug would instead launch
+# a kernel on them, so these tests only run where no GPU is visible.
 FAKE = ctypes.c_void_p(0x10000)
 FAKE_MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+@pytest.fixture
+def fake_ok(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake device pointers are passed only where no GPU is visible")
+    return lib
 
 
 def _attn(lib, m, h_q=32, h_kv=4, d=128, scale=0.088, ps=16, q=FAKE, npages=10):
@@ -268,7 +277,8 @@ def _attn(lib, m, h_q=32, h_kv=4, d=128, scale=0.088, ps=16, q=FAKE, npages=10):
                                npages, ps, FAKE, FAKE, None)
 
 
-def test_attention_validation_fails_closed(lib):
+def test_attention_validation_fails_closed(fake_ok):
+    lib = fake_ok
     m = cpa.meta_build(2, 0, [64], attn_group=8)
     assert _attn(lib, m, h_q=32, h_kv=5) == cpa.CP_ERR_INVALID_ARG        # 32/5: not a multiple
     assert b"multiple" in lib.cp_last_error()
@@ -290,7 +300,8 @@ def test_attention_validation_fails_closed(lib):
                                10, 16, FAKE, FAKE, None) == cpa.CP_ERR_INVALID_ARG
 
 
-def test_copy_validation_fails_closed(lib):
+def test_copy_validation_fails_closed(fake_ok):
+    lib = fake_ok
     m = cpa.meta_build(2, 0, [64], attn_group=8)
     ag = cpa.allgather_meta_build(64, 64, 64, 8)
     assert lib.cp_zigzag_rerange(FAKE, ctypes.byref(m.c), 2, FAKE, FAKE, 256, None) == cpa.CP_ERR_INVALID_ARG
@@ -306,6 +317,47 @@ def test_copy_validation_fails_closed(lib):
     # 2^31-byte rows: 16 rows of 16-byte vectors per workgroup would pass int32
     assert sc(FAKE, ctypes.byref(m.c), FAKE, FAKE, FAKE, FAKE, 8, 16, 1 << 15, 1 << 15, FAKE, FAKE, None) == \
         cpa.CP_ERR_OVERFLOW
+
+
+def test_grids_past_the_work_item_limit_fail_closed(fake_ok):
+    lib = fake_ok
+    """HIP refuses a grid of more than 2^32-1 work-items; the calls return
+    CP_ERR_OVERFLOW on the host before any launch (no GPU needed)."""
+    m = cpa.meta_build(2, 0, [64], attn_group=8)          # 4 chunks of 16 rows
+    # rerange: 16-row chunks of 2^33-byte rows = 2^23 16-KiB parts each, 2^25 in all
+    assert lib.cp_zigzag_rerange(FAKE, ctypes.byref(m.c), 0, FAKE, FAKE, 1 << 33, None) == cpa.CP_ERR_OVERFLOW
+    assert b"grid too large" in lib.cp_last_error()
+    # attention: n_work * H_kv workgroups of 512 threads; 2^23 of them is one too many
+    big = cpa.meta_build(2, 0, [64], attn_group=8)
+    big.c.n_work = (1 << 23) // 8
+    rc = lib.cp_prefill_attn(FAKE, FAKE, FAKE, FAKE, 64, 8, 128, ctypes.c_float(0.088), FAKE,
+                             ctypes.byref(big.c), 4, 16, FAKE, FAKE, None)
+    assert rc == cpa.CP_ERR_OVERFLOW and b"grid too large" in lib.cp_last_error()
+    big.c.n_work = (1 << 23) // 8 - 1    # one workgroup under the limit passes validation
+    big.c.n_work = 0                     # (and is not launched here: an empty grid returns CP_OK)
+    assert lib.cp_prefill_attn(FAKE, FAKE, FAKE, FAKE, 64, 8, 128, ctypes.c_float(0.088), FAKE,
+                               ctypes.byref(big.c), 4, 16, FAKE, FAKE, None) == cpa.CP_OK
+
+
+def test_meta_buffers_are_reused_across_builds():
+    """The staging a caller keeps (MetaBuffers) is reused build after build:
+    no new buffer once it is large enough, and the device view always holds
+    the latest blob.  (On the CPU the 'device' buffer is host memory.)"""
+    mb = cpa.MetaBuffers(device="cpu", capacity=256)
+    first = cpa.meta_build(8, 3, [131072], attn_group=8, buffers=mb)
+    grown = mb.grow_count
+    ptr = first.d_blob.data_ptr()
+    for r in range(8):
+        m = cpa.meta_build(8, r, [131072], attn_group=8, buffers=mb)
+        assert m.d_blob.data_ptr() == ptr and mb.grow_count == grown
+        assert np.array_equal(m.d_blob.numpy(), m.blob)
+    ag = cpa.allgather_meta_build(8192, 8192, 30000, 4, buffers=mb)
+    assert ag.d_blob.data_ptr() == ptr and np.array_equal(ag.d_blob.numpy(), ag.blob)
+    # a larger blob grows the buffers once, then they are reused again
+    big = cpa.meta_build(8, 0, [131072] * 64, attn_group=1, buffers=mb)
+    assert mb.grow_count == grown + 1 and mb.capacity >= big.blob.size
+    again = cpa.meta_build(8, 0, [131072] * 64, attn_group=1, buffers=mb)
+    assert mb.grow_count == grown + 1 and np.array_equal(again.d_blob.numpy(), again.blob)
 
 
 def test_binding_refuses_cpu_tensors():

@@ -59,12 +59,55 @@ def test_traffic_reported_only_for_its_source_workload_and_rank(tmp_path, monkey
     inc = tmp_path / "tables.h"
     inc.write_text("tables")
     sha = hashlib.sha256(b"kernel sourcetables").hexdigest()
-    (tmp_path / "profiles").mkdir()
-    rec = {"kernel_sha256": sha, "workload": "long_cp8_s131072_r3", "rank": 3, "bytes_per_launch": 123}
-    (tmp_path / "profiles" / "attn_traffic.json").write_text(json.dumps(rec))
-    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    assert bench.traffic_for([str(src), str(inc)], "long_cp8_s131072_r3", 3) == 123
-    assert bench.traffic_for([str(src), str(inc)], "long_cp8_s131072_r3", 2) is None
-    assert bench.traffic_for([str(src), str(inc)], "gqa_cp2_s8192", 3) is None
+    rec = {"workload": "long_cp8_s131072_r3", "rank": 3,
+           "kernels": {"attn_kernel": {"kernel_sha256": sha, "bytes_per_launch": 123}}}
+    path = tmp_path / "traffic.json"
+    path.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "TRAFFIC_PATH", str(path))
+    monkeypatch.setitem(bench.KERNEL_SRC, "attn_kernel", [str(src), str(inc)])
+    assert bench.traffic_for("attn_kernel", "long_cp8_s131072_r3", 3) == 123
+    assert bench.traffic_for("attn_kernel", "long_cp8_s131072_r3", 2) is None
+    assert bench.traffic_for("attn_kernel", "gqa_cp2_s8192", 3) is None
+    assert bench.traffic_for("scatter_kernel", "long_cp8_s131072_r3", 3) is None   # not recorded
     src.write_text("kernel source, changed")
-    assert bench.traffic_for([str(src), str(inc)], "long_cp8_s131072_r3", 3) is None
+    assert bench.traffic_for("attn_kernel", "long_cp8_s131072_r3", 3) is None
+
+
+def _counter_csv(path, rows):
+    import csv
+    path.parent.mkdir(parents=True, exist_ok=True)
+    with open(path, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writerows(rows)
+
+
+def test_record_traffic_scales_counters_by_the_copy_calibration(tmp_path, monkeypatch):
+    """Four rocprofv3 --pmc CSVs -> bytes per launch = FETCH_SIZE * (1 GiB /
+    copy FETCH_SIZE) + WRITE_SIZE * (1 GiB / copy WRITE_SIZE), per kernel,
+    averaged over dispatches, each record stamped with its source hash."""
+    kib = 1 << 20
+    _counter_csv(tmp_path / "f" / "x" / "run_counter_collection.csv",
+                 [(1, "void cpattn::attn_kernel<128, 1>(A)", "FETCH_SIZE", 1000.0),
+                  (2, "void cpattn::attn_kernel<128, 1>(A)", "FETCH_SIZE", 3000.0),
+                  (3, "cpattn::rerange_kernel(...)", "FETCH_SIZE", 500.0),
+                  (4, "cpattn::scatter_kernel(...)", "FETCH_SIZE", 700.0)])
+    _counter_csv(tmp_path / "w" / "run_counter_collection.csv",
+                 [(1, "void cpattn::attn_kernel<128, 1>(A)", "WRITE_SIZE", 100.0),
+                  (3, "cpattn::rerange_kernel(...)", "WRITE_SIZE", 400.0),
+                  (4, "cpattn::scatter_kernel(...)", "WRITE_SIZE", 800.0)])
+    _counter_csv(tmp_path / "cf" / "run_counter_collection.csv",
+                 [(1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", kib / 2)])
+    _counter_csv(tmp_path / "cw" / "run_counter_collection.csv",
+                 [(1, "__amd_rocclr_copyBuffer", "WRITE_SIZE", kib)])
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_PATH", str(out))
+    bench.record_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"),
+                         str(tmp_path / "cw"), "long_cp8_s131072_r3", 3)
+    rec = json.loads(out.read_text())
+    assert rec["copy_calibration"]["fetch_factor"] == 2.0 and rec["copy_calibration"]["write_factor"] == 1.0
+    k = rec["kernels"]
+    assert k["attn_kernel"]["bytes_per_launch"] == (2000.0 * 2 + 100.0) * 1024
+    assert k["rerange_kernel"]["bytes_per_launch"] == (500.0 * 2 + 400.0) * 1024
+    assert k["scatter_kernel"]["bytes_per_launch"] == (700.0 * 2 + 800.0) * 1024
+    assert k["attn_kernel"]["kernel_sha256"] == bench.kernel_sha256(bench.KERNEL_SRC["attn_kernel"])

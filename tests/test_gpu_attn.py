@@ -80,7 +80,24 @@ def test_config4_long_cp8_s131072_rank3_sampled_and_properties():
     assert torch.isfinite(got).all()
     vmax = max(float(c.v_seqs[0].abs().max()), 1e-6)
     assert float(got.abs().max()) <= vmax * (1 + 2 ** -7)
-    rows = gc.sample_rows(c.meta_o, c.meta.q_tile, 8, seed=4)[:24]
+    # Every row (all 64 heads) of four whole work items: the first and last
+    # item of each half.  The last next-half item (local rows 16352-16383)
+    # is the 1664-tile diagonal item the longest-first list sends out first;
+    # the last prev-half item holds that half's diagonal.  Plus 64 random
+    # rows, 32 in each half.
+    q_tile = c.meta.q_tile
+    n_prev = c.meta.total_q_prev_tokens
+    n_loc = c.meta.n_local_rows
+    items = [0, n_prev - q_tile, n_prev, n_loc - q_tile]
+    assert q_tile == 32 and items == [0, 8160, 8192, 16352]
+    rows = set()
+    for r0 in items:
+        rows.update(range(r0, r0 + q_tile))
+    rng = np.random.default_rng(4)
+    rows.update(int(x) for x in rng.integers(0, n_prev, 32))
+    rows.update(int(x) for x in rng.integers(n_prev, n_loc, 32))
+    rows = sorted(rows)
+    assert len(rows) >= 4 * 32 + 60
     ref = gc.oracle_rows(c, rows)
     print("cfg4", len(rows), "rows, err", gc.assert_close(got[rows], ref, "cfg4"), flush=True)
     # determinism: a second launch gives identical bits
@@ -363,3 +380,34 @@ def test_random_midsize_sweep_sampled(seed):
     print("midsize", seed, "cp", cp, "lens", lens, "prefix", prefix, "heads", h_q, h_kv, "d", d, "ps", ps,
           flush=True)
     _prefix_extend_case(cp, lens, prefix, h_q, h_kv, d, ps, 6000 + seed, sample=6)
+
+
+def test_meta_buffers_reused_without_allocation_and_stream_ordered():
+    """Metadata uploaded through one reusable MetaBuffers, alternating ranks
+    with no synchronisation between the launches: every launch reads the
+    metadata built for it (stream order), the outputs are bit-identical to
+    those with freshly allocated metadata, and no torch allocation happens
+    once the buffers exist."""
+    w = W["tiny_cp2_s256"]
+    cases = [gc.zigzag_case(w, r) for r in w.ranks]
+    ref = [gc.run_attn(c) for c in cases]
+    mb = cpa.MetaBuffers("cuda")
+    outs = [torch.empty_like(c.q_local) for c in cases]
+    lens = cases[0].lens
+    group = w.h_q // w.h_kv
+
+    def one_round():
+        for r, c in enumerate(cases):
+            m = cpa.meta_build(w.cp_size, c.rank, lens, attn_group=group, buffers=mb)
+            outs[r].fill_(float("nan"))
+            cpa.prefill_attn(c.q_local, c.k_pool, c.v_pool, outs[r], m, c.scale, c.extra["page_size"],
+                             c.indptr, c.indices)
+    one_round()
+    torch.cuda.synchronize()
+    allocs = torch.cuda.memory_stats()["allocation.all.allocated"]
+    for _ in range(5):
+        one_round()
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_stats()["allocation.all.allocated"] == allocs
+    for r in range(len(cases)):
+        assert torch.equal(outs[r].view(torch.int16), ref[r].view(torch.int16)), f"rank {r}"
