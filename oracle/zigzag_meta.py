@@ -1,15 +1,28 @@
 """Zigzag context-parallel metadata, plain Python integers (test oracle).
 
-Follows [P5] (sglang zigzag.py source page): the block layout in its module
-docstring, ``ZigzagCPStrategy.can_apply`` for validity, and
-``ZigzagCPStrategy.build_metadata`` for every list.  Written from the
-definitions, step by step, in the pages' names.
+Written from the block layout that the module docstring of [P5] (sglang
+zigzag.py source page) prints: every sequence is cut into 2*cp_size blocks
+and rank r owns block r (its early block) and block 2*cp_size-1-r (its late
+block); after the all-gather the blocks are reranged to their original order.
+This module does not transcribe the page's ``build_metadata`` formulas.  It
+simulates the layout on the tokens themselves:
+
+  1. cut each sequence into blocks (the one rule taken from ``build_metadata``:
+     the remainder of length / 2cp goes one token each to the first blocks);
+  2. tag every token with (sequence, block, position);
+  3. shard: rank r keeps the tokens of its early blocks of all sequences,
+     then those of its late blocks;
+  4. all-gather: the ranks' shards one after the other;
+and reads every list of ``ZigzagContextParallelMetadata`` off those simulated
+buffers (run lengths, run positions, last positions).  The page's own
+formulas serve only as pins, in tests/test_oracle_meta.py.
 
 Readings where the page leaves a step open:
   * ``num_tokens`` smaller than the sum of extend lengths is rejected (the page
     only handles a surplus, which goes to the last sequence).
-  * Validation follows ``can_apply``: cp_size >= 2, num_tokens >= 2*cp_size,
-    and every extend length >= 2*cp_size; in addition 0 <= cp_rank < cp_size.
+  * Applicability is [P5] ``can_apply``'s condition, read as "every one of the
+    2*cp_size blocks of every sequence gets at least one token, on at least
+    two ranks"; in addition 0 <= cp_rank < cp_size.
 """
 
 from __future__ import annotations
@@ -51,14 +64,13 @@ class ZigzagMeta:
 
 
 def can_apply(cp_size: int, num_tokens: int, extend_lens: Optional[List[int]]) -> bool:
-    """[P5] can_apply: zigzag CP needs at least two ranks and every sequence
-    (and the whole batch) long enough to give each of the 2*cp_size blocks
-    at least one token."""
-    if cp_size <= 1 or num_tokens < 2 * cp_size:
+    """[P5] can_apply: zigzag needs two or more ranks, and every block of the
+    batch and of each sequence must hold at least one token (2*cp_size
+    blocks)."""
+    nblk = 2 * cp_size
+    if cp_size < 2 or num_tokens < nblk:
         return False
-    if extend_lens is None:
-        return True
-    return all(int(x) >= 2 * cp_size for x in extend_lens)
+    return extend_lens is None or min(int(x) for x in extend_lens) >= nblk
 
 
 def _blocks_of(length: int, nblocks: int) -> List[int]:
@@ -69,10 +81,22 @@ def _blocks_of(length: int, nblocks: int) -> List[int]:
     return [base + (1 if j < rem else 0) for j in range(nblocks)]
 
 
+def _runs(tags):
+    """Maximal runs of equal consecutive tags: [(tag, length), ...]."""
+    out = []
+    for t in tags:
+        if out and out[-1][0] == t:
+            out[-1][1] += 1
+        else:
+            out.append([t, 1])
+    return [(t, n) for t, n in out]
+
+
 def build(cp_size: int, cp_rank: int, num_tokens: int,
           seq_lens: Optional[List[int]] = None,
           extend_lens: Optional[List[int]] = None) -> ZigzagMeta:
-    """Metadata of rank ``cp_rank`` for one batch ([P5] build_metadata)."""
+    """Metadata of rank ``cp_rank`` for one batch, read off a simulated shard
+    and all-gather of the batch's tokens ([P5] module docstring layout)."""
     if not (0 <= cp_rank < cp_size):
         raise NotApplicable(f"cp_rank {cp_rank} outside [0, {cp_size})")
     if extend_lens is None:
@@ -82,76 +106,70 @@ def build(cp_size: int, cp_rank: int, num_tokens: int,
         raise NotApplicable("zigzag CP does not apply to this batch")
     seqs = None if seq_lens is None else [int(x) for x in seq_lens]
 
-    # Surplus tokens of the batch belong to the last sequence (and lengthen its
-    # full length by the same amount, so its cached prefix does not change).
+    # Rows of the batch beyond the sequences' extend tokens are counted as
+    # tokens of the last sequence (whose full length grows with them, so its
+    # cached prefix stays the same).
     surplus = int(num_tokens) - sum(ext)
     if surplus < 0:
         raise NotApplicable("num_tokens is smaller than the sum of extend lengths")
-    if surplus > 0:
-        ext[-1] += surplus
-        if seqs is not None and len(seqs) == len(ext):
-            seqs[-1] += surplus
+    ext[-1] += surplus
+    if seqs is not None and len(seqs) == len(ext):
+        seqs[-1] += surplus
 
     bs = len(ext)
     nblk = 2 * cp_size
     # Tokens already in the KV cache ahead of each sequence's extend part.
-    if seqs is not None and len(seqs) == bs:
-        prefix = [max(seqs[b] - ext[b], 0) for b in range(bs)]
-    else:
-        prefix = [0] * bs
-
+    has_seqs = seqs is not None and len(seqs) == bs
+    prefix = [max(seqs[b] - ext[b], 0) if has_seqs else 0 for b in range(bs)]
     blk = [_blocks_of(L, nblk) for L in ext]
-    split_list = [s for b in range(bs) for s in blk[b]]
 
-    # Rank r' holds block r' (its early block) and block 2cp-1-r' (its late
-    # block) of every sequence.
-    def early(rk: int) -> int:
-        return rk
+    # Every token of the batch, in original order: (sequence, block, position).
+    tokens = []
+    for b in range(bs):
+        t = 0
+        for j in range(nblk):
+            for _ in range(blk[b][j]):
+                tokens.append((b, j, t))
+                t += 1
 
-    def late(rk: int) -> int:
-        return nblk - 1 - rk
+    # Shard: rank r keeps its early block (r) of every sequence, then its
+    # late block (2cp-1-r) of every sequence, each in token order.
+    of_block = {}
+    for tk in tokens:
+        of_block.setdefault(tk[:2], []).append(tk)
 
-    per_rank = [sum(blk[b][early(rk)] + blk[b][late(rk)] for b in range(bs))
-                for rk in range(cp_size)]
+    def shard(r):
+        early = [tk for b in range(bs) for tk in of_block[(b, r)]]
+        late = [tk for b in range(bs) for tk in of_block[(b, nblk - 1 - r)]]
+        return early, late
+
+    shards = [shard(r) for r in range(cp_size)]
+    local = [e + l for e, l in shards]
+    gathered = [tk for r in range(cp_size) for tk in local[r]]    # the all-gather, pads left out
+
+    # Chunks: the runs of one (sequence, block) in original token order.
+    chunks = _runs((b, j) for b, j, _t in tokens)
+    chunk_id = {tag: c for c, (tag, _n) in enumerate(chunks)}
+    split_list = [n for _tag, n in chunks]
+    per_rank = [len(x) for x in local]
     max_rank_len = [max(per_rank)] * cp_size
+    zigzag_index = [chunk_id[tag] for tag, _n in _runs((b, j) for b, j, _t in local[cp_rank])]
+    g_runs = _runs((b, j) for b, j, _t in gathered)
+    reverse_split_len = [n for _tag, n in g_runs]
+    g_pos = {tag: k for k, (tag, _n) in enumerate(g_runs)}
+    cp_reverse_index = [g_pos[tag] for tag, _n in chunks]
 
-    # A rank's local rows: the early blocks of all sequences, then the late
-    # blocks of all sequences.  Chunk ids index the split_list chunks.
-    def local_chunks(rk: int) -> List[int]:
-        return ([b * nblk + early(rk) for b in range(bs)] +
-                [b * nblk + late(rk) for b in range(bs)])
-
-    zigzag_index = local_chunks(cp_rank)
-
-    # The all-gathered buffer holds the ranks' local rows one rank after the
-    # other.  Its chunk k is therefore chunk gathered_order[k] of the original
-    # split; cp_reverse_index lists, for each original chunk in order, where
-    # it sits in the gathered buffer.
-    gathered_order = [c for rk in range(cp_size) for c in local_chunks(rk)]
-    where = {c: k for k, c in enumerate(gathered_order)}
-    cp_reverse_index = [where[c] for c in range(bs * nblk)]
-    reverse_split_len = [split_list[c] for c in gathered_order]
-
-    # Each local block attends to every token of its sequence up to and
-    # including itself, after the cached prefix.
-    kv_len_prev = [prefix[b] + sum(blk[b][: early(cp_rank) + 1]) for b in range(bs)]
-    kv_len_next = [prefix[b] + sum(blk[b][: late(cp_rank) + 1]) for b in range(bs)]
-    q_prev = [blk[b][early(cp_rank)] for b in range(bs)]
-    q_next = [blk[b][late(cp_rank)] for b in range(bs)]
-    cu_prev = [0]
-    for x in q_prev:
-        cu_prev.append(cu_prev[-1] + x)
-    cu_next = [0]
-    for x in q_next:
-        cu_next.append(cu_next[-1] + x)
-
-    total = sum(ext)
-    # The page's own consistency checks.
-    assert len(split_list) == bs * nblk
-    assert sum(split_list) == total
-    assert len(zigzag_index) == 2 * bs
-    assert sorted(cp_reverse_index) == list(range(bs * nblk))
-    assert sum(per_rank) == total
+    # This rank's halves: each local block attends to its sequence up to and
+    # including its own last token, after the cached prefix.
+    early, late = shards[cp_rank]
+    q_prev = [sum(1 for tk in early if tk[0] == b) for b in range(bs)]
+    q_next = [sum(1 for tk in late if tk[0] == b) for b in range(bs)]
+    kv_len_prev = [prefix[b] + 1 + max(t for bb, _j, t in early if bb == b) for b in range(bs)]
+    kv_len_next = [prefix[b] + 1 + max(t for bb, _j, t in late if bb == b) for b in range(bs)]
+    cu_prev, cu_next = [0], [0]
+    for b in range(bs):
+        cu_prev.append(cu_prev[-1] + q_prev[b])
+        cu_next.append(cu_next[-1] + q_next[b])
 
     return ZigzagMeta(
         cp_size=cp_size, cp_rank=cp_rank, bs=bs, extend_lens=ext,
@@ -162,9 +180,8 @@ def build(cp_size: int, cp_rank: int, num_tokens: int,
         kv_len_next=kv_len_next, q_prev=q_prev, q_next=q_next,
         cu_seqlens_q_prev=cu_prev, cu_seqlens_q_next=cu_next,
         total_q_prev_tokens=cu_prev[-1], total_q_next_tokens=cu_next[-1],
-        max_seqlen_q_prev=max(q_prev) if q_prev else 0,
-        max_seqlen_q_next=max(q_next) if q_next else 0,
-        total_seq_lens=total,
+        max_seqlen_q_prev=max(q_prev), max_seqlen_q_next=max(q_next),
+        total_seq_lens=len(tokens),
     )
 
 

@@ -205,3 +205,48 @@ def test_can_apply_boundaries(cp, ntok, lens, ok):
     """The zigzag strategy's applicability ([P5] can_apply) at its exact
     boundaries: every one of the 2*cp blocks must get at least one token."""
     assert zigzag_meta.can_apply(cp, ntok, lens) is ok
+
+
+def _page_formulas(cp, r, lens, prefix):
+    """The lists as the build_metadata formulas of the sglang zigzag.py
+    source page state them (block sizes per sequence; per-rank counts from
+    blocks r and 2cp-1-r; the kept chunk ids as two strided ranges; the
+    gathered chunk sizes rank by rank; kv lengths as prefix sums of block
+    sizes).  Used only to pin the oracle, which simulates the token walk."""
+    n = 2 * cp
+    bs = len(lens)
+    blk = [[L // n + (1 if j < L % n else 0) for j in range(n)] for L in lens]
+    per_rank = [sum(bb[k] + bb[n - 1 - k] for bb in blk) for k in range(cp)]
+    zz = list(range(r, r + bs * n, n)) + list(range(n - r - 1, bs * n, n))
+    rsl = []
+    for k in range(cp):
+        rsl += [blk[b][k] for b in range(bs)] + [blk[b][n - 1 - k] for b in range(bs)]
+    kvp = [prefix[b] + sum(blk[b][:r + 1]) for b in range(bs)]
+    kvn = [prefix[b] + sum(blk[b][:n - r]) for b in range(bs)]
+    return dict(split_list=[x for bb in blk for x in bb], per_rank_actual_token=per_rank,
+                zigzag_index=zz, reverse_split_len=rsl, kv_len_prev=kvp, kv_len_next=kvn,
+                q_prev=[blk[b][r] for b in range(bs)], q_next=[blk[b][n - r - 1] for b in range(bs)])
+
+
+def test_token_walk_agrees_with_the_page_formulas():
+    """The simulated shard/all-gather reproduces every list the page's
+    formulas give, over random uneven, multi-sequence, prefixed batches, and
+    satisfies the page's own consistency checks."""
+    rng = random.Random(11)
+    for cp in (2, 3, 4, 5, 8):
+        for _ in range(12):
+            bs, lens = _random_batch(rng, cp)
+            prefix = [rng.choice([0, 0, 3, 29]) for _ in range(bs)]
+            seq = [p + e for p, e in zip(prefix, lens)]
+            for r in range(cp):
+                m = zigzag_meta.build(cp, r, sum(lens), seq_lens=seq, extend_lens=lens)
+                for key, want in _page_formulas(cp, r, lens, prefix).items():
+                    assert getattr(m, key) == want, (cp, r, lens, key)
+                # the page's consistency checks
+                n = 2 * cp
+                assert len(m.split_list) == bs * n and sum(m.split_list) == m.total_seq_lens
+                assert len(m.zigzag_index) == 2 * bs and len(m.cp_reverse_index) == bs * n
+                assert sorted(m.cp_reverse_index) == list(range(bs * n))
+                assert sum(m.per_rank_actual_token) == m.total_seq_lens
+                assert m.cu_seqlens_q_prev == [0] + list(itertools.accumulate(m.q_prev))
+                assert m.cu_seqlens_q_next == [0] + list(itertools.accumulate(m.q_next))

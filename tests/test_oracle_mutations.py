@@ -36,21 +36,24 @@ MUTATIONS = [
     ("oracle/zigzag_meta.py", "return [base + (1 if j < rem else 0) for j in range(nblocks)]",
      "return [base + (1 if j >= nblocks - rem else 0) for j in range(nblocks)]",
      "block remainder on the last blocks"),
-    ("oracle/zigzag_meta.py", "kv_len_next = [prefix[b] + sum(blk[b][: late(cp_rank) + 1]) for b in range(bs)]",
-     "kv_len_next = [prefix[b] + sum(blk[b][: late(cp_rank)]) for b in range(bs)]",
+    ("oracle/zigzag_meta.py",
+     "kv_len_next = [prefix[b] + 1 + max(t for bb, _j, t in late if bb == b) for b in range(bs)]",
+     "kv_len_next = [prefix[b] + min(t for bb, _j, t in late if bb == b) for b in range(bs)]",
      "kv_len_next without its own block"),
-    ("oracle/zigzag_meta.py", "kv_len_prev = [prefix[b] + sum(blk[b][: early(cp_rank) + 1]) for b in range(bs)]",
-     "kv_len_prev = [sum(blk[b][: early(cp_rank) + 1]) for b in range(bs)]",
+    ("oracle/zigzag_meta.py",
+     "kv_len_prev = [prefix[b] + 1 + max(t for bb, _j, t in early if bb == b) for b in range(bs)]",
+     "kv_len_prev = [1 + max(t for bb, _j, t in early if bb == b) for b in range(bs)]",
      "kv_len_prev without the cached prefix"),
-    ("oracle/zigzag_meta.py", """        return ([b * nblk + early(rk) for b in range(bs)] +
-                [b * nblk + late(rk) for b in range(bs)])""",
-     """        return [c for b in range(bs) for c in (b * nblk + early(rk), b * nblk + late(rk))]""",
+    ("oracle/zigzag_meta.py", "    local = [e + l for e, l in shards]",
+     "    local = [[tk for b in range(bs) for tk in of_block[(b, r)] + of_block[(b, nblk - 1 - r)]]\n"
+     "             for r in range(cp_size)]",
      "local rows interleaved per sequence"),
-    ("oracle/zigzag_meta.py", "        ext[-1] += surplus", "        ext[0] += surplus",
+    ("oracle/zigzag_meta.py", "    ext[-1] += surplus", "    ext[0] += surplus",
      "surplus tokens to the first sequence"),
-    ("oracle/zigzag_meta.py", "prefix = [max(seqs[b] - ext[b], 0) for b in range(bs)]",
-     "prefix = [max(seqs[b], 0) for b in range(bs)]", "prefix taken as the full length"),
-    ("oracle/zigzag_meta.py", "        return nblk - 1 - rk", "        return (nblk - 1 - rk + 1) % nblk",
+    ("oracle/zigzag_meta.py", "prefix = [max(seqs[b] - ext[b], 0) if has_seqs else 0 for b in range(bs)]",
+     "prefix = [max(seqs[b], 0) if has_seqs else 0 for b in range(bs)]", "prefix taken as the full length"),
+    ("oracle/zigzag_meta.py", "of_block[(b, nblk - 1 - r)]]\n        return early, late",
+     "of_block[(b, (nblk - r) % nblk)]]\n        return early, late",
      "late block index shifted"),
     ("oracle/layout.py", "return np.concatenate([chunks[i] for i in meta.cp_reverse_index], axis=0)",
      "return np.concatenate([chunks[i] for i in sorted(meta.cp_reverse_index)], axis=0)",
