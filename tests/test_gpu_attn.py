@@ -411,3 +411,35 @@ def test_meta_buffers_reused_without_allocation_and_stream_ordered():
     assert torch.cuda.memory_stats()["allocation.all.allocated"] == allocs
     for r in range(len(cases)):
         assert torch.equal(outs[r].view(torch.int16), ref[r].view(torch.int16)), f"rank {r}"
+
+
+@pytest.mark.parametrize("gap,what", [(40.0, "~650 above the first block"),
+                                      (6.125, "~100 above the first block")])
+def test_late_keys_far_above_the_first_block(gap, what):
+    """Scores of later keys far above every score of the item's first key
+    block, which sets the softmax reference.  With q = 1 and k = gap in every
+    dimension the score is 128 * gap / sqrt(128) above the first block's
+    (k = 0): about 650 in the exp2 domain for gap 40 (the probabilities
+    against the old reference would overflow fp32, so the lazy reference
+    must be raised, and O and l rescaled, mid-item) and about 100 for gap
+    6.125.  Both must match the oracle."""
+    cp, lens, h_q, h_kv, d, ps = 2, [512], 4, 1, 128, 16
+    total = sum(lens)
+    qg, kg, vg = synth.normal_bf16(77, (total, h_q, d), (total, h_kv, d), (total, h_kv, d))
+    kg[:64] = 0.0                    # the first key tile scores 0 against any query
+    qg[:] = 1.0
+    kg[100:110] = gap                # a few keys far above it, early in the sequence
+    kg[400:404] = gap                # and late
+    base = synth.Workload(name="gap", seed=77, causal=True, h_q=h_q, h_kv=h_kv, d=d, page_size=ps,
+                          contiguous_kv=True, cp_size=cp, ranks=(0, 1), bs=1)
+    for r in range(cp):
+        c = gc.zigzag_case(base, r, lens=lens)
+        mo = c.meta_o
+        from oracle import layout
+        c.q_local = torch.from_numpy(layout.shard(gc.bits(qg), mo)).view(torch.bfloat16).cuda()
+        c.k_seqs, c.v_seqs = [kg], [vg]
+        c.k_pool = kg.view(total // ps, ps, h_kv, d).cuda()
+        c.v_pool = vg.view(total // ps, ps, h_kv, d).cuda()
+        got = gc.run_attn(c)
+        ref = oatt.zigzag_rank(c.q_local.cpu(), c.k_seqs, c.v_seqs, mo, c.scale)
+        print(what, "rank", r, "err", gc.assert_close(got, ref, f"gap {gap} rank {r}"), flush=True)
