@@ -284,12 +284,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   auto issue_tile = [&](int t, auto stc, const Pages& pg) {
     unsigned char* kd = kbuf(stc);
     unsigned char* vd = vbuf(stc);
-    // Common case (a tile within one page): every key of the tile is real
-    // and its page id valid, so each address is a wave-uniform base plus a
-    // per-lane constant.
+    // Common case: every key of the tile is real and its page id valid, and
+    // the tile lies in one page or runs on into the next pool page (adjacent
+    // pages, as a contiguous K/V tensor read through the identity table
+    // gives), so each address is a wave-uniform base plus a per-lane constant.
     const int first = kv0 + t * kAttnKeys;   // page-table position of the tile's key 0
     if (PAGE_PER_TILE && (t + 1) * kAttnKeys <= s.kv_len && pg.p[0] >= 0 && pg.p[0] < a.num_pages &&
-        (first & ps_mask) + kAttnKeys <= ps_mask + 1) {
+        ((first & ps_mask) + kAttnKeys <= ps_mask + 1 || (pg.p[1] == pg.p[0] + 1 && pg.p[1] < a.num_pages))) {
       // wave-uniform tile base (scalar registers) plus a 32-bit per-lane
       // offset: the loads take the scalar-base address form, no vector adds
       const uint64_t base =
