@@ -281,6 +281,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   uint32_t ld_const[LOADS];
 #pragma unroll
   for (int u = 0; u < LOADS; ++u) ld_const[u] = (uint32_t)ld_row[u] * tok_stride + ld_lane[u];
+  // The same from the first key row of the lane's wave instruction, for the
+  // group modes, whose base moves to that row's page.
+  constexpr int kRowsPerLoad = 1024 / ROW_BYTES;
+  static_assert(GP == 0 || GP % kRowsPerLoad == 0, "a wave instruction's rows lie in one page");
+  uint32_t ld_gconst[LOADS];
+#pragma unroll
+  for (int u = 0; u < LOADS; ++u)
+    ld_gconst[u] = (uint32_t)(ld_row[u] - (u * kWaves + wave) * kRowsPerLoad) * tok_stride + ld_lane[u];
   auto issue_tile = [&](int t, auto stc, const Pages& pg) {
     unsigned char* kd = kbuf(stc);
     unsigned char* vd = vbuf(stc);
@@ -305,6 +313,37 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
             (__attribute__((address_space(3))) void*)&vd[(u * kWaves + wave) * 1024], 16, 0, 0);
       }
       return;
+    }
+    if constexpr (GP != 0) {
+      // Group modes: the rows of one wave instruction lie in one page (GP is
+      // a multiple of the rows it covers), so with all keys real and the
+      // pages valid each load is again a scalar base plus a per-lane constant.
+      if ((t + 1) * kAttnKeys <= s.kv_len) {
+        int pu[LOADS];
+        bool ok = true;
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+          const int j = (u * kWaves + wave) * kRowsPerLoad / GP;   // wave-uniform
+          int pj = pg.p[0];
+#pragma unroll
+          for (int i = 1; i < NPP; ++i) pj = j == i ? pg.p[i] : pj;
+          pu[u] = pj;
+          ok = ok && pj >= 0 && pj < a.num_pages;
+        }
+        if (ok) {
+#pragma unroll
+          for (int u = 0; u < LOADS; ++u) {
+            const int row0 = (u * kWaves + wave) * kRowsPerLoad;
+            const uint64_t base =
+                (((uint64_t)pu[u] << shift) | (uint32_t)((first + row0) & ps_mask)) * tok_stride;
+            __builtin_amdgcn_global_load_lds(a.k_pool + base + (int64_t)ld_gconst[u],
+                (__attribute__((address_space(3))) void*)&kd[(u * kWaves + wave) * 1024], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(a.v_pool + base + (int64_t)ld_gconst[u],
+                (__attribute__((address_space(3))) void*)&vd[(u * kWaves + wave) * 1024], 16, 0, 0);
+          }
+          return;
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
