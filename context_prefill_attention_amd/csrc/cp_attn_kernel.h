@@ -197,9 +197,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   const int n_tiles = w.n_tiles;
   // first tile that holds a key past some row's limit
   const int t_mask = min(n_tiles, max(0, (item_limit + 1) / kAttnKeys));
-  // Tiles the pipeline runs: n_tiles rounded up to 1 + a multiple of the
-  // ring depth (see the main loop); tiles past n_tiles hold no visible key.
-  const int n_pad = n_tiles > 0 ? 1 + ((n_tiles + 2) & ~3) : 0;
 
   bf16x8 qop[KSTEPS];
 #pragma unroll
@@ -384,7 +381,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   // compiler may place them before or after the loads of tile t+1, so none
   // of them is counted as allowed to stay outstanding.
   auto wait_tile = [&](int t) {
-    if (t + 1 < n_pad) wait_vmcnt<2 * LOADS>();
+    if (t + 1 < n_tiles) wait_vmcnt<2 * LOADS>();
     else wait_vmcnt<0>();
   };
 
@@ -442,9 +439,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   // block in pb (8 registers of packed bf16 pairs, C-element order).  Two
   // 16-key steps; step kk uses C elements 8*kk .. 8*kk+7 of the block, i.e.
   // keys 32*kb + 16*kk + 8*(i/4) + 4*half + i%4 for operand slot i.
-  auto pv_blk = [&](auto stc, auto kbc, const uint32_t* pb) {
+  auto pv_at = [&](unsigned char* vt, auto kbc, const uint32_t* pb) {
     constexpr int kb = decltype(kbc)::value;
-    unsigned char* vt = vbuf(stc);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int kst = kb * 2 + kk;
@@ -461,6 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       }
     }
   };
+  auto pv_blk = [&](auto stc, auto kbc, const uint32_t* pb) { pv_at(vbuf(stc), kbc, pb); };
   // Keys of block kb of tile t past each row's limit leave the scores.
   auto mask_blk = [&](int t, int kb, f32x16& sb) {
     const int rel = limit - t * kAttnKeys - kb * 32 - half * 4;   // visible key offsets within the block
@@ -554,7 +551,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     Pages pg0 = fetch_pages(0), pg1 = fetch_pages(1);
     issue_tile(0, I0{}, pg0);
     Pages pg_next = fetch_pages(2);
-    if (n_pad > 1) issue_tile(1, I1{}, pg1);
+    if (n_tiles > 1) issue_tile(1, I1{}, pg1);
     wait_tile(0);
     step_barrier();
 
@@ -562,7 +559,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     // Step 0: no previous tile.
     {
       const Pages pg_after = fetch_pages(3);
-      if (2 < n_pad) issue_tile(2, I2{}, pg_next);
+      if (2 < n_tiles) issue_tile(2, I2{}, pg_next);
       pg_next = pg_after;
       f32x16 s0 = qk_blk(I0{}, I0{});
       s1 = qk_blk(I0{}, I1{});
@@ -581,7 +578,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       constexpr bool MASKED = decltype(maskc)::value;
       using SP = std::integral_constant<int, (st + kStages - 1) % kStages>;   // stage of tile t-1
       const Pages pg_after = fetch_pages(t + 3);
-      if (t + 2 < n_pad) issue_tile(t + 2, std::integral_constant<int, (st + 2) % kStages>{}, pg_next);
+      if (t + 2 < n_tiles) issue_tile(t + 2, std::integral_constant<int, (st + 2) % kStages>{}, pg_next);
       pg_next = pg_after;
       // A wave still in half 1 outranks one already in half 2 for the
       // SIMD's issue slots, so the wave that lags catches up before the
@@ -603,27 +600,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     int t = 1;
     const int t_full_end = max(1, t_mask);          // tiles [1, t_mask) need no mask
     // Both loops are unrolled by the ring depth, so every stage index is a
-    // constant and each loop body is a single path.  After the first, t % 4
-    // == 1; the second runs the remaining tiles (a few fully visible ones,
-    // which the mask leaves unchanged, then the diagonal) up to n_pad, and
-    // its padding tiles are fully masked.  The last tile, n_pad - 1, is then
-    // always in stage 0.
+    // constant.  After the first, t % 4 == 1; the second runs the remaining
+    // tiles (a few fully visible ones, which the mask leaves unchanged, then
+    // the diagonal) four at a time, and the last 0-3 tiles follow one by one.
     for (; t + 3 < t_full_end; t += 4) {
       step(I1{}, std::false_type{}, t);
       step(I2{}, std::false_type{}, t + 1);
       step(I3{}, std::false_type{}, t + 2);
       step(I0{}, std::false_type{}, t + 3);
     }
-    for (; t < n_pad; t += 4) {
+    for (; t + 3 < n_tiles; t += 4) {
       step(I1{}, std::true_type{}, t);
       step(I2{}, std::true_type{}, t + 1);
       step(I3{}, std::true_type{}, t + 2);
       step(I0{}, std::true_type{}, t + 3);
     }
-    // The last tile's PV products and its block-1 softmax.
-    pv_blk(I0{}, I0{}, pk);
+    if (t < n_tiles) step(I1{}, std::true_type{}, t);
+    if (t + 1 < n_tiles) step(I2{}, std::true_type{}, t + 1);
+    if (t + 2 < n_tiles) step(I3{}, std::true_type{}, t + 2);
+    // The last tile's PV products and its block-1 softmax, from its stage.
+    const int st_last = (n_tiles - 1) & (kStages - 1);
+    unsigned char* v_last = st_last == 0 ? v_s0 : st_last == 1 ? v_s1 : st_last == 2 ? v_s2 : v_s3;
+    pv_at(v_last, I0{}, pk);
     sm_blk(s1, pk + 8);
-    pv_blk(I0{}, I1{}, pk + 8);
+    pv_at(v_last, I1{}, pk + 8);
   }
 
   // Epilogue: O = O^T / l.  Lane (col, half) holds d = 32*db + 8*(j/4) + 4*half + j%4.
