@@ -294,22 +294,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     // pages, as a contiguous K/V tensor read through the identity table
     // gives), so each address is a wave-uniform base plus a per-lane constant.
     const int first = kv0 + t * kAttnKeys;   // page-table position of the tile's key 0
-    if (PAGE_PER_TILE && (t + 1) * kAttnKeys <= s.kv_len && pg.p[0] >= 0 && pg.p[0] < a.num_pages &&
-        ((first & ps_mask) + kAttnKeys <= ps_mask + 1 || (pg.p[1] == pg.p[0] + 1 && pg.p[1] < a.num_pages))) {
-      // wave-uniform tile base (scalar registers) plus a 32-bit per-lane
-      // offset: the loads take the scalar-base address form, no vector adds
-      const uint64_t base =
-          (((uint64_t)pg.p[0] << shift) | (uint32_t)(first & ps_mask)) * tok_stride;
-      const unsigned char* k_base = a.k_pool + base;
-      const unsigned char* v_base = a.v_pool + base;
+    if constexpr (PAGE_PER_TILE) {
+      if ((t + 1) * kAttnKeys <= s.kv_len && pg.p[0] >= 0 && pg.p[0] < a.num_pages &&
+          ((first & ps_mask) + kAttnKeys <= ps_mask + 1 || (pg.p[1] == pg.p[0] + 1 && pg.p[1] < a.num_pages))) {
+        // wave-uniform tile base (scalar registers) plus a 32-bit per-lane
+        // offset: the loads take the scalar-base address form, no vector adds
+        const uint64_t base =
+            (((uint64_t)pg.p[0] << shift) | (uint32_t)(first & ps_mask)) * tok_stride;
+        const unsigned char* k_base = a.k_pool + base;
+        const unsigned char* v_base = a.v_pool + base;
 #pragma unroll
-      for (int u = 0; u < LOADS; ++u) {
-        __builtin_amdgcn_global_load_lds(k_base + (int64_t)ld_const[u],
-            (__attribute__((address_space(3))) void*)&kd[(u * kWaves + wave) * 1024], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(v_base + (int64_t)ld_const[u],
-            (__attribute__((address_space(3))) void*)&vd[(u * kWaves + wave) * 1024], 16, 0, 0);
+        for (int u = 0; u < LOADS; ++u) {
+          __builtin_amdgcn_global_load_lds(k_base + (int64_t)ld_const[u],
+              (__attribute__((address_space(3))) void*)&kd[(u * kWaves + wave) * 1024], 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(v_base + (int64_t)ld_const[u],
+              (__attribute__((address_space(3))) void*)&vd[(u * kWaves + wave) * 1024], 16, 0, 0);
+        }
+        return;
       }
-      return;
     }
     if constexpr (GP != 0) {
       // Group modes: the rows of one wave instruction lie in one page (GP is
