@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
     if constexpr (PAGE_PER_TILE) {
       const int e0 = (kv0 + min(t, n_tiles - 1) * kAttnKeys) >> shift;
       pg.p[0] = entry(e0);
-      pg.p[1] = straddle ? entry(e0 + 1) : pg.p[0];
+      pg.p[1] = entry(straddle ? e0 + 1 : e0);   // an address choice: nothing waits for pg.p[0] here
     } else if constexpr (GP != 0) {
       const int e0 = (kv0 + min(t, n_tiles - 1) * kAttnKeys) >> shift;
 #pragma unroll
