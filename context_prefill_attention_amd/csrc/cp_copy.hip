@@ -10,11 +10,14 @@
 // (materialize_full_kv writes the full-sequence K/V at the extend tokens'
 // cache locations).
 //
-// Launch shape: a 1-D grid; each workgroup owns one fixed-size byte range
-// (16 KiB) of one chunk (rerange) or of one page run of a chunk (scatter), so
-// its lookups are a few divisions and no search.  Each lane moves 16-byte
-// vectors with several loads in flight before the stores, which is what
-// keeps HBM3E busy.
+// Launch shape: a 1-D grid; each workgroup owns one fixed-size byte range of
+// one chunk (rerange, 16 KiB) or of one page run of a chunk (scatter, 2 KiB
+// of K and 2 KiB of V), so its lookups are a few divisions and no search.
+// Each lane moves 16-byte vectors with its loads in flight before the
+// stores.  The scatter's small workgroups keep many pool pages in flight at
+// once, which pays when the pages are written in random order (measured:
+// 16 KiB ranges ran 11 % slower with a permuted page table, 5 % with the
+// identity table).
 #include <hip/hip_runtime.h>
 
 #include "../../include/cpattn.h"
@@ -28,6 +31,8 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;                                   // 16-B vectors per lane in flight
 constexpr int64_t kCopyBytesPerWG = 16LL * kCopyThreads * kCopyUnroll;   // 16 KiB
+constexpr int kScatterThreads = 128;                              // one 16-B vector of K and of V per lane
+constexpr int64_t kScatterBytesPerWG = 16LL * kScatterThreads;   // 2 KiB
 
 // One workgroup copies bytes [part*16KiB, (part+1)*16KiB) of chunk c.
 __global__ __launch_bounds__(kCopyThreads) void rerange_kernel(
@@ -81,11 +86,11 @@ __global__ __launch_bounds__(kCopyThreads) void rerange_narrow_kernel(
 // Scatter.  Within one chunk, the tokens that share a pool page are a
 // contiguous run of rows on both sides: consecutive rows of the gathered
 // buffer and consecutive slots of that page.  The grid is laid out as
-// (chunk, j-th page the chunk touches, 16 KiB slice of that run), so a
+// (chunk, j-th page the chunk touches, 2 KiB slice of that run), so a
 // workgroup copies one contiguous byte range of K and of V, with a single
 // page-table lookup, exactly like the rerange.  Workgroups whose slice lies
 // past the end of their run exit at once.
-__global__ __launch_bounds__(kCopyThreads) void scatter_kernel(
+__global__ __launch_bounds__(kScatterThreads) void scatter_kernel(
     const Chunk* __restrict__ chunks, int32_t pages_per_chunk, int32_t slices_per_page,
     const unsigned char* __restrict__ kg, const unsigned char* __restrict__ vg,
     unsigned char* __restrict__ kp, unsigned char* __restrict__ vp, int64_t row_bytes,
@@ -104,7 +109,7 @@ __global__ __launch_bounds__(kCopyThreads) void scatter_kernel(
   const int64_t hi = min((int64_t)ch.pos0 + ch.n_rows, page_first + page_size);
   if (lo >= hi) return;
   const int64_t nbytes = (int64_t)(hi - lo) * row_bytes;
-  const int64_t start = (int64_t)slice * kCopyBytesPerWG;
+  const int64_t start = (int64_t)slice * kScatterBytesPerWG;
   if (start >= nbytes) return;
   // the page id: an entry outside the sequence's row of the table, or an id
   // outside the pool, leaves its slots untouched (nothing is written)
@@ -114,28 +119,18 @@ __global__ __launch_bounds__(kCopyThreads) void scatter_kernel(
   if (page < 0 || page >= num_pages) return;
   const int64_t src_off = ((int64_t)ch.g_row + (lo - ch.pos0)) * row_bytes + start;
   const int64_t dst_off = ((int64_t)page * page_size + (lo - page_first)) * row_bytes + start;
-  const int64_t avail = nbytes - start;
-  u32x4 a[kCopyUnroll], b[kCopyUnroll];
-#pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
-    const int64_t off = (int64_t)(u * kCopyThreads + threadIdx.x) * 16;
-    if (off < avail) {
-      a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kg + src_off + off));
-      b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + src_off + off));
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
-    const int64_t off = (int64_t)(u * kCopyThreads + threadIdx.x) * 16;
-    if (off < avail) {
-      __builtin_nontemporal_store(a[u], reinterpret_cast<u32x4*>(kp + dst_off + off));
-      __builtin_nontemporal_store(b[u], reinterpret_cast<u32x4*>(vp + dst_off + off));
-    }
+  const int64_t off = (int64_t)threadIdx.x * 16;
+  if (off < nbytes - start) {
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kg + src_off + off));
+    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + src_off + off));
+    __builtin_nontemporal_store(a, reinterpret_cast<u32x4*>(kp + dst_off + off));
+    __builtin_nontemporal_store(b, reinterpret_cast<u32x4*>(vp + dst_off + off));
   }
 }
 
 // HIP rejects a launch whose grid holds more than 2^32-1 work-items.
 constexpr int64_t kMaxCopyGrid = 4294967295LL / kCopyThreads;
+constexpr int64_t kMaxScatterGrid = 4294967295LL / kScatterThreads;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -204,18 +199,18 @@ extern "C" int cp_kv_scatter(const void* d_blob, const cp_meta_t* meta,
   if (!aligned16(k_gathered) || !aligned16(v_gathered) || !aligned16(k_pool) || !aligned16(v_pool))
     return set_error(CP_ERR_INVALID_ARG, "K/V buffers must be 16-byte aligned");
   // A chunk of n rows touches at most ceil((n - 1) / ps) + 1 pages; a page's
-  // run is at most ps rows, i.e. ceil(ps * row_bytes / 16 KiB) slices.
+  // run is at most ps rows, i.e. ceil(ps * row_bytes / 2 KiB) slices.
   const int64_t pages_per_chunk =
       meta->max_chunk_rows > 0 ? (meta->max_chunk_rows - 1 + page_size - 1) / page_size + 1 : 0;
-  const int64_t slices_per_page = ((int64_t)page_size * row_bytes + kCopyBytesPerWG - 1) / kCopyBytesPerWG;
+  const int64_t slices_per_page = ((int64_t)page_size * row_bytes + kScatterBytesPerWG - 1) / kScatterBytesPerWG;
   const int64_t grid = pages_per_chunk * slices_per_page * meta->n_chunks;
   if (pages_per_chunk > 2147483647LL || slices_per_page > 2147483647LL ||
-      pages_per_chunk * slices_per_page > 2147483647LL || grid > kMaxCopyGrid)
+      pages_per_chunk * slices_per_page > 2147483647LL || grid > kMaxScatterGrid)
     return set_error(CP_ERR_OVERFLOW, "scatter grid too large (%lld workgroups of %d threads)",
-                     (long long)grid, kCopyThreads);
+                     (long long)grid, kScatterThreads);
   if (grid == 0) return CP_OK;
   const Chunk* chunks = reinterpret_cast<const Chunk*>(static_cast<const char*>(d_blob) + meta->off_chunks);
-  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)grid), dim3(kCopyThreads), 0, stream, chunks,
+  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)grid), dim3(kScatterThreads), 0, stream, chunks,
                      (int32_t)pages_per_chunk, (int32_t)slices_per_page,
                      static_cast<const unsigned char*>(k_gathered),
                      static_cast<const unsigned char*>(v_gathered), static_cast<unsigned char*>(k_pool),
