@@ -12,12 +12,13 @@
 //
 // Launch shape: a 1-D grid; each workgroup owns one fixed-size byte range of
 // one chunk (rerange, 16 KiB) or of one page run of a chunk (scatter, 2 KiB
-// of K and 2 KiB of V), so its lookups are a few divisions and no search.
-// Each lane moves 16-byte vectors with its loads in flight before the
-// stores.  The scatter's small workgroups keep many pool pages in flight at
-// once, which pays when the pages are written in random order (measured:
-// 16 KiB ranges ran 11 % slower with a permuted page table, 5 % with the
-// identity table).
+// of K and the same 2 KiB of V), so its lookups are a few divisions and no
+// search.  Each lane moves 16-byte vectors with its loads in flight before
+// the stores.  The scatter's small ranges keep many pool pages in flight at
+// once, which pays when the pages are written in random order, and half of
+// its lanes copy K while the other half copy V (measured against 16 KiB
+// ranges of K and V per workgroup: 18 % faster with a permuted page table,
+// 9 % with the identity table).
 #include <hip/hip_runtime.h>
 
 #include "../../include/cpattn.h"
@@ -31,8 +32,8 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;                                   // 16-B vectors per lane in flight
 constexpr int64_t kCopyBytesPerWG = 16LL * kCopyThreads * kCopyUnroll;   // 16 KiB
-constexpr int kScatterThreads = 128;                              // one 16-B vector of K and of V per lane
-constexpr int64_t kScatterBytesPerWG = 16LL * kScatterThreads;   // 2 KiB
+constexpr int kScatterThreads = 256;      // lanes 0-127 copy K, 128-255 the same bytes of V
+constexpr int64_t kScatterBytesPerWG = 16LL * (kScatterThreads / 2);   // 2 KiB of each
 
 // One workgroup copies bytes [part*16KiB, (part+1)*16KiB) of chunk c.
 __global__ __launch_bounds__(kCopyThreads) void rerange_kernel(
@@ -119,12 +120,14 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(
   if (page < 0 || page >= num_pages) return;
   const int64_t src_off = ((int64_t)ch.g_row + (lo - ch.pos0)) * row_bytes + start;
   const int64_t dst_off = ((int64_t)page * page_size + (lo - page_first)) * row_bytes + start;
-  const int64_t off = (int64_t)threadIdx.x * 16;
+  constexpr int kHalf = kScatterThreads / 2;
+  const bool is_v = threadIdx.x >= kHalf;
+  const int64_t off = (int64_t)(threadIdx.x - (is_v ? kHalf : 0)) * 16;
+  const unsigned char* src = is_v ? vg : kg;
+  unsigned char* dst = is_v ? vp : kp;
   if (off < nbytes - start) {
-    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kg + src_off + off));
-    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + src_off + off));
-    __builtin_nontemporal_store(a, reinterpret_cast<u32x4*>(kp + dst_off + off));
-    __builtin_nontemporal_store(b, reinterpret_cast<u32x4*>(vp + dst_off + off));
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + src_off + off));
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(dst + dst_off + off));
   }
 }
 

@@ -217,8 +217,8 @@ int cp_zigzag_rerange(const void* d_blob, const cp_meta_t* meta, int32_t directi
  * Errors: NULL meta or d_blob, meta kind not zigzag (or another version),
  * H_kv < 1, D < 1, page_size < 1, num_pages < 1, NULL or misaligned pointers
  * -> CP_ERR_INVALID_ARG; H_kv*D*2 not a multiple of 16 -> CP_ERR_UNSUPPORTED;
- * a grid of more than 2^25-1 workgroups (one per 2 KiB of a page run of a
- * chunk: HIP's 2^32-1 work-item limit at 128 threads) -> CP_ERR_OVERFLOW;
+ * a grid of more than 2^24-1 workgroups (one per 2 KiB of a page run of a
+ * chunk: HIP's 2^32-1 work-item limit at 256 threads) -> CP_ERR_OVERFLOW;
  * launch failure -> CP_ERR_HIP.
  */
 int cp_kv_scatter(const void* d_blob, const cp_meta_t* meta,
