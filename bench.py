@@ -313,6 +313,7 @@ _CSRC = os.path.join(ROOT, "context_prefill_attention_amd", "csrc")
 KERNEL_SRC = {
     "attn_kernel": [os.path.join(_CSRC, f) for f in ("cp_attn_kernel.h", "cp_internal.h")],
     "rerange_kernel": [os.path.join(_CSRC, f) for f in ("cp_copy.hip", "cp_internal.h")],
+    "rerange_pair_kernel": [os.path.join(_CSRC, f) for f in ("cp_copy.hip", "cp_internal.h")],
     "scatter_kernel": [os.path.join(_CSRC, f) for f in ("cp_copy.hip", "cp_internal.h")],
 }
 
@@ -355,8 +356,7 @@ def run_zigzag(args, w, torch, cpa, synth) -> dict:
         cpa.kv_scatter(meta, k_gd, v_gd, k_pool, v_pool, w.page_size, ip, ix)
         if ev:
             ev[1].record()
-        cpa.zigzag_rerange(meta, k_gd, k_orig, cpa.GATHERED_TO_ORIG)
-        cpa.zigzag_rerange(meta, v_gd, v_orig, cpa.GATHERED_TO_ORIG)
+        cpa.zigzag_rerange_kv(meta, k_gd, k_orig, v_gd, v_orig, cpa.GATHERED_TO_ORIG)
         if ev:
             ev[2].record()
         cpa.prefill_attn(q_d, k_pool, v_pool, out, meta, scale, w.page_size, ip, ix)
@@ -375,13 +375,13 @@ def run_zigzag(args, w, torch, cpa, synth) -> dict:
     res["attn_ms_median"] = round(float(sorted(per["attn"])[len(per["attn"]) // 2]), 4)
     res["torch_allocations_in_timed_steps"] = run_timed.allocations
     roofline = res.pop("roofline")
-    rer_t, sc_t = traffic_for("rerange_kernel", w.name, rank), traffic_for("scatter_kernel", w.name, rank)
+    rer_t, sc_t = traffic_for("rerange_pair_kernel", w.name, rank), traffic_for("scatter_kernel", w.name, rank)
     res.update({
         "rerange_kv_ms": round(ph["rerange"], 4),
         "rerange_gbps": round(rerange_bytes / (ph["rerange"] * 1e-3) / 1e9, 1),
         "rerange_frac_of_hbm_peak": round(rerange_bytes / (ph["rerange"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        # one rerange launch moves K or V: algorithmic bytes vs the counters
-        "rerange_bytes_per_launch": {"algorithmic": rerange_bytes // 2, "counters": rer_t},
+        # one rerange launch moves K and V: algorithmic bytes vs the counters
+        "rerange_bytes_per_launch": {"algorithmic": rerange_bytes, "counters": rer_t},
         "scatter_kv_ms": round(ph["scatter"], 4),
         "scatter_gbps": round(scatter_bytes / (ph["scatter"] * 1e-3) / 1e9, 1),
         "scatter_frac_of_hbm_peak": round(scatter_bytes / (ph["scatter"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

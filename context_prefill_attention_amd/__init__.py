@@ -20,7 +20,7 @@ import numpy as np
 
 __all__ = [
     "CpError", "Meta", "MetaBuffers", "meta_build", "allgather_meta_build", "allgather_packed_meta_build", "zigzag_rerange",
-    "kv_scatter", "prefill_attn", "load_library", "LIB_PATH",
+    "zigzag_rerange_kv", "kv_scatter", "prefill_attn", "load_library", "LIB_PATH",
     "GATHERED_TO_ORIG", "ORIG_TO_GATHERED",
 ]
 
@@ -81,12 +81,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.cp_allgather_meta_build.argtypes = [_i32, _i32, _i32, _i32, _vp, _i64, P(CMeta)]
     lib.cp_allgather_packed_meta_build.argtypes = [_i32, P(_i32), _i32, _i32, _i32, _vp, _i64, P(CMeta)]
     lib.cp_zigzag_rerange.argtypes = [_vp, P(CMeta), _i32, _vp, _vp, _i64, _vp]
+    lib.cp_zigzag_rerange_kv.argtypes = [_vp, P(CMeta), _i32, _vp, _vp, _vp, _vp, _i64, _vp]
     lib.cp_kv_scatter.argtypes = [_vp, P(CMeta), _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                   _vp, _vp, _vp]
     lib.cp_prefill_attn.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, ctypes.c_float, _vp,
                                     P(CMeta), _i32, _i32, _vp, _vp, _vp]
     for fn in ("cp_meta_build", "cp_allgather_meta_build", "cp_allgather_packed_meta_build",
-               "cp_zigzag_rerange", "cp_kv_scatter", "cp_prefill_attn"):
+               "cp_zigzag_rerange", "cp_zigzag_rerange_kv", "cp_kv_scatter", "cp_prefill_attn"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.cp_last_error.restype = ctypes.c_char_p
     lib.cp_last_error.argtypes = []
@@ -330,6 +331,31 @@ def zigzag_rerange(meta: Meta, src, dst, direction: int = GATHERED_TO_ORIG) -> N
                                           f"dst {dst.shape[0]} (want {rows_dst})")
     _check(lib.cp_zigzag_rerange(_need_device(meta), ctypes.byref(meta.c), direction,
                                  _dev_tensor(src, "src"), _dev_tensor(dst, "dst"), row_bytes, _stream()))
+
+
+def _rerange_rows(meta: Meta, src, dst, direction: int) -> int:
+    row_bytes = src.element_size() * (src.numel() // max(src.shape[0], 1))
+    if dst.element_size() * (dst.numel() // max(dst.shape[0], 1)) != row_bytes or src.dtype != dst.dtype:
+        raise CpError(CP_ERR_INVALID_ARG, "src and dst rows differ")
+    n_g = meta.cp_size * meta.max_rank_len
+    rows_src, rows_dst = (n_g, meta.total_seq_lens) if direction == GATHERED_TO_ORIG else \
+        (meta.total_seq_lens, n_g)
+    if src.shape[0] != rows_src or dst.shape[0] != rows_dst:
+        raise CpError(CP_ERR_INVALID_ARG, f"rows: src {src.shape[0]} (want {rows_src}), "
+                                          f"dst {dst.shape[0]} (want {rows_dst})")
+    return row_bytes
+
+
+def zigzag_rerange_kv(meta: Meta, k_src, k_dst, v_src, v_dst, direction: int = GATHERED_TO_ORIG) -> None:
+    """``cp_zigzag_rerange_kv`` on the current stream: K and V in one launch."""
+    lib = load_library()
+    row_bytes = _rerange_rows(meta, k_src, k_dst, direction)
+    if _rerange_rows(meta, v_src, v_dst, direction) != row_bytes:
+        raise CpError(CP_ERR_INVALID_ARG, "K and V rows differ")
+    _check(lib.cp_zigzag_rerange_kv(_need_device(meta), ctypes.byref(meta.c), direction,
+                                    _dev_tensor(k_src, "k_src"), _dev_tensor(k_dst, "k_dst"),
+                                    _dev_tensor(v_src, "v_src"), _dev_tensor(v_dst, "v_dst"),
+                                    row_bytes, _stream()))
 
 
 def kv_scatter(meta: Meta, k_gathered, v_gathered, k_pool, v_pool, page_size: int,

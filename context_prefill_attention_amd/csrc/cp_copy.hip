@@ -62,6 +62,41 @@ __global__ __launch_bounds__(kCopyThreads) void rerange_kernel(
   }
 }
 
+// K and V together (rows a multiple of 16 bytes): the same chunk/part split
+// with parts of kPairBytesPerWG; half the lanes copy the part's bytes of K,
+// the other half the same bytes of V, so one launch moves both tensors.
+constexpr int kPairUnroll = 1;
+constexpr int64_t kPairBytesPerWG = 16LL * (kCopyThreads / 2) * kPairUnroll;   // 2 KiB of each
+__global__ __launch_bounds__(kCopyThreads) void rerange_pair_kernel(
+    const Chunk* __restrict__ chunks, int32_t parts_per_chunk, int32_t forward,
+    const unsigned char* __restrict__ k_src, unsigned char* __restrict__ k_dst,
+    const unsigned char* __restrict__ v_src, unsigned char* __restrict__ v_dst, int64_t row_bytes) {
+  constexpr int kHalf = kCopyThreads / 2;
+  const int c = blockIdx.x / parts_per_chunk;
+  const int part = blockIdx.x - c * parts_per_chunk;
+  const Chunk ch = chunks[c];
+  const int64_t nbytes = (int64_t)ch.n_rows * row_bytes;
+  const int64_t start = (int64_t)part * kPairBytesPerWG;
+  if (start >= nbytes) return;
+  const int64_t g_off = (int64_t)ch.g_row * row_bytes, o_off = (int64_t)ch.o_row * row_bytes;
+  const bool is_v = threadIdx.x >= kHalf;
+  const int lane = threadIdx.x - (is_v ? kHalf : 0);
+  const unsigned char* s = (is_v ? v_src : k_src) + (forward ? g_off : o_off) + start;
+  unsigned char* d = (is_v ? v_dst : k_dst) + (forward ? o_off : g_off) + start;
+  const int64_t avail = nbytes - start;
+  u32x4 v[kPairUnroll];
+#pragma unroll
+  for (int u = 0; u < kPairUnroll; ++u) {
+    const int64_t off = (int64_t)(u * kHalf + lane) * 16;
+    if (off < avail) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(s + off));
+  }
+#pragma unroll
+  for (int u = 0; u < kPairUnroll; ++u) {
+    const int64_t off = (int64_t)(u * kHalf + lane) * 16;
+    if (off < avail) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(d + off));
+  }
+}
+
 // Rows whose size is not a multiple of 16 bytes (positions, narrow
 // per-token tensors): the same chunk/part split, copied in elements of T,
 // the widest power of two up to 8 bytes that divides the row size, so every
@@ -176,6 +211,40 @@ extern "C" int cp_zigzag_rerange(const void* d_blob, const cp_meta_t* meta, int3
     hipLaunchKernelGGL(rerange_narrow_kernel<uint16_t>, g, b, 0, stream, chunks, (int32_t)parts, fwd, sp, dp, row_bytes);
   else
     hipLaunchKernelGGL(rerange_narrow_kernel<uint8_t>, g, b, 0, stream, chunks, (int32_t)parts, fwd, sp, dp, row_bytes);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(CP_ERR_HIP, "rerange launch: %s", hipGetErrorString(e));
+  return CP_OK;
+}
+
+extern "C" int cp_zigzag_rerange_kv(const void* d_blob, const cp_meta_t* meta, int32_t direction,
+                                    const void* k_src, void* k_dst, const void* v_src, void* v_dst,
+                                    int64_t row_bytes, hipStream_t stream) {
+  clear_error();
+  if (!meta || !d_blob) return set_error(CP_ERR_INVALID_ARG, "meta or d_blob is NULL");
+  if (meta->version != CP_META_VERSION || meta->kind != CP_META_ZIGZAG)
+    return set_error(CP_ERR_INVALID_ARG, "metadata is not zigzag metadata of this version");
+  if (direction != CP_RERANGE_GATHERED_TO_ORIG && direction != CP_RERANGE_ORIG_TO_GATHERED)
+    return set_error(CP_ERR_INVALID_ARG, "direction=%d", direction);
+  if (row_bytes <= 0) return set_error(CP_ERR_INVALID_ARG, "row_bytes=%lld must be positive", (long long)row_bytes);
+  if (!k_src || !k_dst || !v_src || !v_dst) return set_error(CP_ERR_INVALID_ARG, "a K or V pointer is NULL");
+  if (!aligned16(k_src) || !aligned16(k_dst) || !aligned16(v_src) || !aligned16(v_dst))
+    return set_error(CP_ERR_INVALID_ARG, "K and V buffers must be 16-byte aligned");
+  if (row_bytes % 16 != 0) {   // narrow rows: the one-tensor copy, twice
+    if (int rc = cp_zigzag_rerange(d_blob, meta, direction, k_src, k_dst, row_bytes, stream)) return rc;
+    return cp_zigzag_rerange(d_blob, meta, direction, v_src, v_dst, row_bytes, stream);
+  }
+  const int64_t chunk_bytes = (int64_t)meta->max_chunk_rows * row_bytes;
+  const int64_t parts = (chunk_bytes + kPairBytesPerWG - 1) / kPairBytesPerWG;
+  const int64_t grid = parts * meta->n_chunks;
+  if (parts > 2147483647LL || grid > kMaxCopyGrid)
+    return set_error(CP_ERR_OVERFLOW, "rerange grid too large (%lld workgroups of %d threads)",
+                     (long long)grid, kCopyThreads);
+  if (grid == 0) return CP_OK;
+  const Chunk* chunks = reinterpret_cast<const Chunk*>(static_cast<const char*>(d_blob) + meta->off_chunks);
+  hipLaunchKernelGGL(rerange_pair_kernel, dim3((unsigned)grid), dim3(kCopyThreads), 0, stream, chunks,
+                     (int32_t)parts, (int32_t)(direction == CP_RERANGE_GATHERED_TO_ORIG),
+                     static_cast<const unsigned char*>(k_src), static_cast<unsigned char*>(k_dst),
+                     static_cast<const unsigned char*>(v_src), static_cast<unsigned char*>(v_dst), row_bytes);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(CP_ERR_HIP, "rerange launch: %s", hipGetErrorString(e));
   return CP_OK;

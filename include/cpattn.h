@@ -197,6 +197,18 @@ int cp_zigzag_rerange(const void* d_blob, const cp_meta_t* meta, int32_t directi
                       const void* src, void* dst, int64_t row_bytes, hipStream_t stream);
 
 /*
+ * cp_zigzag_rerange_kv -- cp_zigzag_rerange of K and of V in one launch
+ * (gather_kv_cache reranges both after the all-gather, [P5]).  Arguments,
+ * layout, ownership and errors are those of cp_zigzag_rerange, applied to
+ * each of the pairs (k_src -> k_dst) and (v_src -> v_dst), which share
+ * row_bytes; the result is bit-identical to the two separate calls.  Rows
+ * whose size is not a multiple of 16 bytes are copied by those two calls.
+ */
+int cp_zigzag_rerange_kv(const void* d_blob, const cp_meta_t* meta, int32_t direction,
+                         const void* k_src, void* k_dst, const void* v_src, void* v_dst,
+                         int64_t row_bytes, hipStream_t stream);
+
+/*
  * cp_kv_scatter -- gathered K and V rows into the paged KV pool ([P5]
  * materialize_full_kv: gather, rerange, write at the extend tokens' cache
  * locations; [P1]: every rank's pool then holds the full sequence).

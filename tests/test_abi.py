@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol(lib):
     text = open(HEADER).read()
     names = set(re.findall(r"^\s*(?:int|const char\*)\s+(cp_\w+)\s*\(", text, flags=re.M))
     assert {"cp_meta_build", "cp_allgather_meta_build", "cp_allgather_packed_meta_build",
-            "cp_zigzag_rerange", "cp_kv_scatter",
+            "cp_zigzag_rerange", "cp_zigzag_rerange_kv", "cp_kv_scatter",
             "cp_prefill_attn", "cp_last_error", "cp_version"} <= names
     for n in names:
         assert hasattr(lib, n), n   # ctypes dlsym succeeds
@@ -309,6 +309,14 @@ def test_copy_validation_fails_closed(fake_ok):
     assert lib.cp_zigzag_rerange(FAKE, ctypes.byref(m.c), 0, FAKE, FAKE, -4, None) == cpa.CP_ERR_INVALID_ARG
     assert lib.cp_zigzag_rerange(FAKE, ctypes.byref(m.c), 0, FAKE_MISALIGNED, FAKE, 256, None) == cpa.CP_ERR_INVALID_ARG
     assert lib.cp_zigzag_rerange(FAKE, ctypes.byref(ag.c), 0, FAKE, FAKE, 256, None) == cpa.CP_ERR_INVALID_ARG
+    kv = lib.cp_zigzag_rerange_kv
+    assert kv(FAKE, ctypes.byref(m.c), 2, FAKE, FAKE, FAKE, FAKE, 256, None) == cpa.CP_ERR_INVALID_ARG
+    assert kv(FAKE, ctypes.byref(m.c), 0, FAKE, FAKE, FAKE, FAKE, 0, None) == cpa.CP_ERR_INVALID_ARG
+    assert kv(FAKE, ctypes.byref(m.c), 0, FAKE, FAKE, None, FAKE, 256, None) == cpa.CP_ERR_INVALID_ARG
+    assert kv(FAKE, ctypes.byref(m.c), 0, FAKE, FAKE, FAKE, FAKE_MISALIGNED, 256, None) == cpa.CP_ERR_INVALID_ARG
+    assert kv(FAKE, ctypes.byref(ag.c), 0, FAKE, FAKE, FAKE, FAKE, 256, None) == cpa.CP_ERR_INVALID_ARG
+    assert kv(None, ctypes.byref(m.c), 0, FAKE, FAKE, FAKE, FAKE, 256, None) == cpa.CP_ERR_INVALID_ARG
+    assert b"NULL" in lib.cp_last_error()
     sc = lib.cp_kv_scatter
     assert sc(FAKE, ctypes.byref(m.c), FAKE, FAKE, FAKE, FAKE, 8, 16, 1, 4, FAKE, FAKE, None) == cpa.CP_ERR_UNSUPPORTED
     assert sc(FAKE, ctypes.byref(m.c), FAKE, FAKE, FAKE, FAKE, 8, 0, 4, 128, FAKE, FAKE, None) == cpa.CP_ERR_INVALID_ARG
@@ -326,6 +334,9 @@ def test_grids_past_the_work_item_limit_fail_closed(fake_ok):
     m = cpa.meta_build(2, 0, [64], attn_group=8)          # 4 chunks of 16 rows
     # rerange: 16-row chunks of 2^33-byte rows = 2^23 16-KiB parts each, 2^25 in all
     assert lib.cp_zigzag_rerange(FAKE, ctypes.byref(m.c), 0, FAKE, FAKE, 1 << 33, None) == cpa.CP_ERR_OVERFLOW
+    assert b"grid too large" in lib.cp_last_error()
+    assert lib.cp_zigzag_rerange_kv(FAKE, ctypes.byref(m.c), 0, FAKE, FAKE, FAKE, FAKE, 1 << 33, None) == \
+        cpa.CP_ERR_OVERFLOW
     assert b"grid too large" in lib.cp_last_error()
     # attention: n_work * H_kv workgroups of 512 threads; 2^23 of them is one too many
     big = cpa.meta_build(2, 0, [64], attn_group=8)

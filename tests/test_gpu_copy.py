@@ -49,6 +49,38 @@ def test_rerange_both_directions_bit_exact(cp, lens, row_bytes):
     assert np.array_equal(dst2.cpu().numpy(), layout.rerange_inverse(x, mo, blank))
 
 
+@pytest.mark.parametrize("cp,lens,row_bytes", _variants() + [(3, [45, 300], 1), (5, [777, 100], 20), (2, [64], 8)])
+def test_rerange_kv_pair_both_directions_bit_exact(cp, lens, row_bytes):
+    """cp_zigzag_rerange_kv moves K and V in one launch (rows of any width:
+    narrow rows take the one-tensor path twice); both tensors match the
+    oracle in both directions, pads untouched."""
+    total = sum(lens)
+    w = row_bytes // 2 if row_bytes % 2 == 0 else row_bytes
+    dt = np.int16 if row_bytes % 2 == 0 else np.int8
+    rng = np.random.default_rng(7 + len(lens))
+    info = np.iinfo(dt)
+    x = rng.integers(info.min, info.max, size=(total, w), dtype=dt)
+    y = rng.integers(info.min, info.max, size=(total, w), dtype=dt)
+    mo = zigzag_meta.build(cp, 0, total, extend_lens=lens)
+    meta = cpa.meta_build(cp, 0, lens, device="cuda")
+    pad = dt(0x7F) if dt == np.int8 else SENT
+    gx, gy = layout.gathered_buffer(x, mo, pad_value=pad), layout.gathered_buffer(y, mo, pad_value=pad)
+    dx = torch.full((total, w), int(pad), dtype=torch.from_numpy(x).dtype, device="cuda")
+    dy = torch.full_like(dx, int(pad))
+    cpa.zigzag_rerange_kv(meta, torch.from_numpy(gx).cuda(), dx, torch.from_numpy(gy).cuda(), dy,
+                          cpa.GATHERED_TO_ORIG)
+    torch.cuda.synchronize()
+    assert np.array_equal(dx.cpu().numpy(), layout.rerange(gx, mo))
+    assert np.array_equal(dy.cpu().numpy(), layout.rerange(gy, mo))
+    bx, by = np.full_like(gx, 0x12), np.full_like(gy, 0x21)
+    ex, ey = torch.from_numpy(bx).cuda(), torch.from_numpy(by).cuda()
+    cpa.zigzag_rerange_kv(meta, torch.from_numpy(x).cuda(), ex, torch.from_numpy(y).cuda(), ey,
+                          cpa.ORIG_TO_GATHERED)
+    torch.cuda.synchronize()
+    assert np.array_equal(ex.cpu().numpy(), layout.rerange_inverse(x, mo, bx))
+    assert np.array_equal(ey.cpu().numpy(), layout.rerange_inverse(y, mo, by))
+
+
 def _narrow_variants():
     rng = random.Random(23)
     out = [(4, [1024, 777, 4093], rb) for rb in (1, 2, 3, 4, 6, 8, 12, 24, 40)]
@@ -114,6 +146,23 @@ def test_rerange_config4_kv_full_size():
         cpa.zigzag_rerange(meta, torch.from_numpy(g_ref).view(torch.bfloat16).cuda(), dst, cpa.GATHERED_TO_ORIG)
         torch.cuda.synchronize()
         assert np.array_equal(gc.bits(dst), xb)
+
+
+def test_rerange_kv_pair_config4_full_size():
+    """The paired launch on the long-context workload's K and V (the bench step's call)."""
+    w = synth.WORKLOADS["long_cp8_s131072_r3"]
+    total = w.seq_len
+    mo = zigzag_meta.build(w.cp_size, 3, total)
+    meta = cpa.meta_build(w.cp_size, 3, [total], device="cuda")
+    _, k, v = synth.normal_bf16(w.seed, (1, 1, 1), (total, w.h_kv, w.d), (total, w.h_kv, w.d))
+    kb, vb = gc.bits(k), gc.bits(v)
+    gk = torch.from_numpy(layout.gathered_buffer(kb, mo, pad_value=SENT)).view(torch.bfloat16).cuda()
+    gv = torch.from_numpy(layout.gathered_buffer(vb, mo, pad_value=SENT)).view(torch.bfloat16).cuda()
+    dk = torch.empty((total, w.h_kv, w.d), dtype=torch.bfloat16, device="cuda")
+    dv = torch.empty_like(dk)
+    cpa.zigzag_rerange_kv(meta, gk, dk, gv, dv, cpa.GATHERED_TO_ORIG)
+    torch.cuda.synchronize()
+    assert np.array_equal(gc.bits(dk), kb) and np.array_equal(gc.bits(dv), vb)
 
 
 def _scatter_case(cp, lens, h_kv, d, ps, seq=None, seed=0, spare_pages=5):
