@@ -347,7 +347,9 @@ def test_random_packed_allgather_sweep(seed):
             break
         cu.append(cu[-1] + n)
     if rng.random() < 0.5 or len(cu) == 1:
-        cu.append(kv_total - int(rng.integers(0, min(40, kv_total // 4))))
+        end = kv_total - int(rng.integers(0, min(40, kv_total // 4)))   # a pad suffix
+        if end > cu[-1]:
+            cu.append(end)
     h_kv = int(rng.choice([1, 2]))
     h_q = h_kv * int(rng.choice([1, 4, 8]))
     d = int(rng.choice([64, 128]))
