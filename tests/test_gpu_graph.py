@@ -1,4 +1,5 @@
-"""The whole device step (KV scatter, rerange of K and V, fused attention)
+"""The whole device step (KV scatter, rerange of K and V, one tensor at a
+time or both in one launch, fused attention)
 captured in a HIP graph and replayed.
 
 The entry points allocate nothing, never synchronise and launch on the
@@ -20,7 +21,8 @@ from oracle import layout, zigzag_meta
 pytestmark = pytest.mark.gpu
 
 
-def test_step_captured_in_a_graph_replays_bit_exact():
+@pytest.mark.parametrize("paired", [False, True], ids=["rerange_each", "rerange_kv"])
+def test_step_captured_in_a_graph_replays_bit_exact(paired):
     cp, rank, lens, h_q, h_kv, d, ps = 4, 1, [300, 128, 77], 16, 2, 128, 16
     total = sum(lens)
     qg, kg, vg = synth.normal_bf16(71, (total, h_q, d), (total, h_kv, d), (total, h_kv, d))
@@ -43,8 +45,11 @@ def test_step_captured_in_a_graph_replays_bit_exact():
 
     def step():
         cpa.kv_scatter(meta, k_gath, v_gath, kp, vp, ps, ip, ix)
-        cpa.zigzag_rerange(meta, k_gath, k_orig, cpa.GATHERED_TO_ORIG)
-        cpa.zigzag_rerange(meta, v_gath, v_orig, cpa.GATHERED_TO_ORIG)
+        if paired:
+            cpa.zigzag_rerange_kv(meta, k_gath, k_orig, v_gath, v_orig, cpa.GATHERED_TO_ORIG)
+        else:
+            cpa.zigzag_rerange(meta, k_gath, k_orig, cpa.GATHERED_TO_ORIG)
+            cpa.zigzag_rerange(meta, v_gath, v_orig, cpa.GATHERED_TO_ORIG)
         cpa.prefill_attn(q_loc, kp, vp, out, meta, scale, ps, ip, ix)
 
     step()
