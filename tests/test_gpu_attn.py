@@ -445,3 +445,38 @@ def test_late_keys_far_above_the_first_block(gap, what):
         got = gc.run_attn(c)
         ref = oatt.zigzag_rank(c.q_local.cpu(), c.k_seqs, c.v_seqs, mo, c.scale)
         print(what, "rank", r, "err", gc.assert_close(got, ref, f"gap {gap} rank {r}"), flush=True)
+
+
+def test_concurrent_streams_independent():
+    """The library keeps no device state between calls: the whole step of two
+    different shares (metadata, scatter, paired rerange, attention), issued on
+    two streams at once, gives the same bits as one share at a time."""
+    w = W["gqa_cp2_s8192"]
+    cases = [gc.zigzag_case(w, r, q_global=False) for r in w.ranks]
+    ref = [gc.run_attn(c) for c in cases]
+    n_g = w.cp_size * cases[0].meta.max_rank_len
+    total = sum(cases[0].lens)
+    gens = [torch.Generator(device="cuda").manual_seed(90 + i) for i in range(2)]
+    k_gath = [torch.randn(n_g, w.h_kv, w.d, generator=g, device="cuda").to(torch.bfloat16) for g in gens]
+    v_gath = [torch.randn(n_g, w.h_kv, w.d, generator=g, device="cuda").to(torch.bfloat16) for g in gens]
+    ko_ref = [torch.empty(total, w.h_kv, w.d, dtype=torch.bfloat16, device="cuda") for _ in cases]
+    vo_ref = [torch.empty_like(t) for t in ko_ref]
+    for c, kg, vg, ko, vo in zip(cases, k_gath, v_gath, ko_ref, vo_ref):
+        cpa.zigzag_rerange_kv(c.meta, kg, ko, vg, vo, cpa.GATHERED_TO_ORIG)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in cases]
+    outs = [torch.full_like(c.q_local, float("nan")) for c in cases]
+    ko = [torch.full_like(t, float("nan")) for t in ko_ref]
+    vo = [torch.full_like(t, float("nan")) for t in vo_ref]
+    for _ in range(3):
+        for i, (c, s) in enumerate(zip(cases, streams)):
+            with torch.cuda.stream(s):
+                m = cpa.meta_build(w.cp_size, c.rank, c.lens, attn_group=w.h_q // w.h_kv, device="cuda")
+                cpa.zigzag_rerange_kv(m, k_gath[i], ko[i], v_gath[i], vo[i], cpa.GATHERED_TO_ORIG)
+                cpa.prefill_attn(c.q_local, c.k_pool, c.v_pool, outs[i], m, c.scale, c.extra["page_size"],
+                                 c.indptr, c.indices)
+    torch.cuda.synchronize()
+    for i, c in enumerate(cases):
+        assert torch.equal(outs[i].view(torch.int16), ref[i].view(torch.int16)), f"rank {c.rank}"
+        assert torch.equal(ko[i].view(torch.int16), ko_ref[i].view(torch.int16))
+        assert torch.equal(vo[i].view(torch.int16), vo_ref[i].view(torch.int16))
