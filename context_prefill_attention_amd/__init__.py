@@ -48,7 +48,7 @@ class CMeta(ctypes.Structure):
         ("total_q_prev_tokens", _i32), ("total_q_next_tokens", _i32),
         ("max_seqlen_q_prev", _i32), ("max_seqlen_q_next", _i32), ("n_local_rows", _i32),
         ("n_chunks", _i32), ("max_chunk_rows", _i32), ("n_seg", _i32), ("n_work", _i32),
-        ("max_kv_len", _i32), ("q_tile", _i32), ("kv_align", _i32), ("reserved", _i32),
+        ("max_kv_len", _i32), ("q_tile", _i32), ("kv_align", _i32), ("mean_item_tiles", _i32),
         ("blob_bytes", _i64),
         ("off_split_list", _i64), ("off_zigzag_index", _i64), ("off_cp_reverse_index", _i64),
         ("off_reverse_split_len", _i64), ("off_per_rank_actual_token", _i64),
@@ -388,7 +388,9 @@ def prefill_attn(q, k_pool, v_pool, out, meta: Meta, scale: float, page_size: in
 
     q, out: [n_local_rows, H_q, D] bf16; k_pool, v_pool: [num_pages,
     page_size, H_kv, D] bf16 (a contiguous [S, H_kv, D] tensor can be viewed
-    as pages with the identity page table)."""
+    as pages with the identity page table).  The launch uses job counters in
+    the header of ``meta.d_blob`` and leaves them zero, so two attention
+    launches with the same device blob must not run concurrently."""
     import torch
     lib = load_library()
     n, h_q, d = q.shape

@@ -4,7 +4,10 @@
 // work list of the metadata blob.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
+#include <mutex>
+#include <vector>
 
 #include "../../include/cpattn.h"
 #include "cp_attn_kernel.h"
@@ -15,6 +18,30 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Items must average this many key tiles for run-time job hand-out to pay
+// for its ticket (one device-scope atomic before a workgroup's first load).
+constexpr int kDynamicMinTiles = 48;
+
+// Compute units of the current device, queried once per device.
+int compute_units(int* n_cu) {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(CP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= (int)cache.size()) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || n < 1)
+      return set_error(CP_ERR_HIP, "compute-unit count of device %d: %s", dev, hipGetErrorString(e));
+    cache[dev] = n;
+  }
+  *n_cu = cache[dev];
+  return CP_OK;
+}
+
 }  // namespace
 }  // namespace cpattn
 
@@ -22,7 +49,7 @@ using namespace cpattn;
 
 extern "C" int cp_prefill_attn(const void* q, const void* k_pool, const void* v_pool, void* out,
                                int32_t H_q, int32_t H_kv, int32_t D, float scale,
-                               const void* d_blob, const cp_meta_t* meta,
+                               void* d_blob, const cp_meta_t* meta,
                                int32_t num_pages, int32_t page_size, const int32_t* kv_page_indptr,
                                const int32_t* kv_page_indices, hipStream_t stream) {
   clear_error();
@@ -49,18 +76,34 @@ extern "C" int cp_prefill_attn(const void* q, const void* k_pool, const void* v_
     return set_error(CP_ERR_INVALID_ARG, "a device pointer is NULL");
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
     return set_error(CP_ERR_INVALID_ARG, "q, k_pool, v_pool and out must be 16-byte aligned");
+  // One job per (work item, KV head).  Jobs [0, n_static) go to workgroups
+  // [0, n_static); with run-time scheduling the other workgroups take the
+  // remaining jobs from the blob's counters, and n_spare more let the faster
+  // XCDs take more than their share (those that find nothing left end at once).
+  const int64_t n_jobs = (int64_t)meta->n_work * H_kv;
+  if (n_jobs == 0) return CP_OK;
   // HIP rejects a launch whose grid holds more than 2^32-1 work-items.
-  const int64_t grid = (int64_t)meta->n_work * H_kv;
+  if (n_jobs > 4294967295LL / kThreads)
+    return set_error(CP_ERR_OVERFLOW, "attention grid too large (%lld workgroups of %d threads)",
+                     (long long)n_jobs, kThreads);
+  int n_cu = 0;
+  if (int rc = compute_units(&n_cu)) return rc;
+  const bool dynamic = n_jobs > n_cu && meta->mean_item_tiles >= kDynamicMinTiles;
+  const int64_t n_static = dynamic ? n_cu : n_jobs;
+  const int64_t n_spare = dynamic ? std::max<int64_t>(8, (n_jobs - n_static) / 8) : 0;
+  const int64_t grid = n_jobs + n_spare;
   if (grid > 4294967295LL / kThreads)
     return set_error(CP_ERR_OVERFLOW, "attention grid too large (%lld workgroups of %d threads)",
                      (long long)grid, kThreads);
-  if (grid == 0) return CP_OK;
   AttnArgs args;
   args.q = static_cast<const unsigned char*>(q);
   args.k_pool = static_cast<const unsigned char*>(k_pool);
   args.v_pool = static_cast<const unsigned char*>(v_pool);
   args.out = static_cast<unsigned char*>(out);
-  const char* base = static_cast<const char*>(d_blob);
+  char* base = static_cast<char*>(d_blob);
+  args.ctr = reinterpret_cast<unsigned int*>(base + kCtrOffset);
+  args.n_jobs = (int32_t)n_jobs;
+  args.n_static = (int32_t)n_static;
   args.segs = reinterpret_cast<const Seg*>(base + meta->off_segs);
   args.work = reinterpret_cast<const Work*>(base + meta->off_work);
   args.indptr = kv_page_indptr;

@@ -14,11 +14,22 @@
 // Work decomposition.  A workgroup (8 waves, 512 lanes) owns one KV head and
 // 256 (position, query head) rows: q_tile = 256/G consecutive positions times
 // the G query heads that share the KV head, head-minor.  Every K/V tile staged
-// in LDS is therefore used by all G heads of the group.  Workgroup w takes KV
-// head w % H_kv and work item w / H_kv: consecutive workgroups are dispatched
-// round-robin over the 8 XCDs, so with H_kv in {1,2,4,8} each XCD sees one
-// KV head (or a fixed subset) and its 4 MB L2 holds that head's K/V stream.
-// Work items come longest-first from the host.
+// in LDS is therefore used by all G heads of the group.  Job j is KV head
+// j % H_kv of work item j / H_kv; work items come longest-first from the host.
+// Consecutive workgroups are dispatched round-robin over the 8 XCDs, so with
+// H_kv in {1,2,4,8} and job j run on XCD j % 8, each XCD sees one KV head (or
+// a fixed subset) and its 4 MB L2 holds that head's K/V stream.
+//
+// Scheduling.  Workgroup b runs job b (static), or, when the host asks for
+// run-time scheduling, the first round (b < n_static, one per CU) runs job b
+// and every later workgroup takes a ticket: jobs n_static.. are dealt to 8
+// queues, queue q holding n_static + q + 8t in order, and a workgroup draws
+// from the queue of the XCD it runs on, which keeps the head-per-XCD pattern.
+// The XCDs of one chip do not run at one speed (the same tiles take a few
+// per cent longer on some), so with a fixed split the chip waits for its
+// slowest XCD; here an XCD whose queue is empty draws from the next queue
+// with jobs left, and the spare workgroups of the grid give the faster XCDs
+// the slots to do so.
 //
 // Per wave: 32 rows.  Scores are computed transposed, S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 d from LDS, B = Q^T held in
@@ -90,7 +101,44 @@ struct AttnArgs {
   int32_t h_q, h_kv, group, num_pages;
   int32_t page_shift;
   float scale_log2;  // softmax scale * log2(e): scores go through exp2
+  // Run-time scheduling: the job counters in the blob header (queues 0-7 and
+  // the ticket count), the number of jobs and of statically placed ones
+  // (n_static == n_jobs: every workgroup runs its own index, no counters).
+  unsigned int* ctr;
+  int32_t n_jobs, n_static;
 };
+
+// Job of workgroup b; called by all 64 lanes of wave 0, returns the same
+// value in each (-1: nothing left).  Ticket takers draw from the queue of
+// their XCD (hardware register XCC_ID) with one atomic; when it is empty,
+// lanes 0-7 read the 8 queue counters at once and the wave draws from the
+// first queue after its own with jobs left, again until all are empty (each
+// failed draw finds one more queue empty, so at most 8 rounds).
+__device__ __forceinline__ int take_job(unsigned int* ctr, int n_jobs, int n_static, int lane) {
+  const int b = (int)blockIdx.x;
+  if (b < n_static) return b;
+  const int n_dyn = n_jobs - n_static;
+  // jobs of queue q: n_static + q + 8t for t < n_q(q)
+  auto n_q = [&](int q) -> unsigned int { return q < n_dyn ? (unsigned int)(n_dyn - q + 7) / 8u : 0u; };
+  const int x = (int)(__builtin_amdgcn_s_getreg((15 << 11) | (0 << 6) | 20) & 7);   // XCC_ID[3:0]
+  unsigned int t = 0;
+  if (lane == 0 && n_q(x) > 0) t = atomicAdd(&ctr[x], 1u);
+  t = __builtin_amdgcn_readfirstlane(t);
+  if (t < n_q(x)) return n_static + x + 8 * (int)t;
+  for (int round = 0; round < 8; ++round) {
+    unsigned int c = 0xffffffffu;
+    if (lane < 8) c = __hip_atomic_load(&ctr[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t left = __builtin_amdgcn_ballot_w64(lane < 8 && c < n_q(lane));
+    if (left == 0) break;
+    const uint64_t rot = ((left >> x) | (left << (8 - x))) & 0xff;   // bit k: queue (x + k) % 8
+    const int q = (x + (int)__builtin_ctzll(rot)) & 7;
+    unsigned int t2 = 0;
+    if (lane == q) t2 = atomicAdd(&ctr[q], 1u);
+    t2 = __builtin_amdgcn_readlane(t2, q);
+    if (t2 < n_q(q)) return n_static + q + 8 * (int)t2;
+  }
+  return -1;
+}
 
 // 16-byte chunk slot of (row, chunk) inside a row of NC chunks.  For NC = 16
 // the row's low 4 bits are permuted (bits 0-1 to 2-3) and XORed into the
@@ -175,8 +223,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   };
 
   const int h_kv = a.h_kv, group = a.group;
-  const int kvh = blockIdx.x % h_kv;
-  const Work w = a.work[blockIdx.x / h_kv];
+  // Ticket takers also count themselves in ctr[8]; the count's result is only
+  // looked at when this workgroup ends, so its round trip overlaps the job.
+  // The last of them (every draw of this launch is done by then) clears the
+  // counters for the next launch.
+  __shared__ int job_slot;
+  const unsigned int n_takers = gridDim.x - (unsigned int)a.n_static;
+  unsigned int taker_no = 0;   // thread 0 of a ticket taker: 1 + its place in the count
+  if (threadIdx.x < 64) {
+    const int jb = take_job(a.ctr, a.n_jobs, a.n_static, threadIdx.x);
+    if (threadIdx.x == 0) {
+      job_slot = jb;
+      if ((int)blockIdx.x >= a.n_static) taker_no = atomicAdd(&a.ctr[8], 1u) + 1u;
+    }
+  }
+  auto clear_counters = [&]() {
+    if (threadIdx.x == 0 && n_takers != 0u && taker_no == n_takers) {
+#pragma unroll
+      for (int i = 0; i < kCtrWords; ++i)
+        __hip_atomic_store(&a.ctr[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  __syncthreads();
+  const int job = __builtin_amdgcn_readfirstlane(job_slot);
+  if (job < 0) {
+    clear_counters();
+    return;
+  }
+  const int kvh = job % h_kv;
+  const Work w = a.work[job / h_kv];
   const Seg s = a.segs[w.seg];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -629,6 +704,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   }
 
   // Epilogue: O = O^T / l.  Lane (col, half) holds d = 32*db + 8*(j/4) + 4*half + j%4.
+  // (Thread 0 always holds a valid row: it reaches clear_counters below.)
   if (!valid) return;
   const float l_tot = wave_half_sum(l_run);   // the two lane halves summed different keys
   const float inv = live ? 1.f / l_tot : 0.f;
@@ -643,6 +719,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
       v[1] = pack_bf16x2(o[db][jj * 4 + 2] * inv, o[db][jj * 4 + 3] * inv);
       *reinterpret_cast<u32x2*>(orow + d * 2) = v;
     }
+  clear_counters();
 }
 
 }  // namespace

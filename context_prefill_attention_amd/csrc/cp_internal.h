@@ -52,6 +52,14 @@ constexpr int kMaxGroup = kAttnRows;  // H_q / H_kv upper bound (one position pe
 constexpr uint32_t kBlobMagic = 0x31415043u;  // "CPA1"
 constexpr int64_t kBlobAlign = 256;
 
+// Job counters of the attention launch, inside the blob's 256-byte header:
+// words 0-7 are the next place in each of the 8 job queues, word 8 counts the
+// workgroups that have taken a ticket.  The builder writes them as zero and
+// every launch leaves them zero.
+constexpr int64_t kCtrOffset = 128;
+constexpr int kCtrWords = 9;
+static_assert(kCtrOffset + 4 * kCtrWords <= kBlobAlign, "counters fit in the header");
+
 // Error helpers (cp_meta.cpp).
 int set_error(int code, const char* fmt, ...);
 void clear_error();

@@ -56,6 +56,7 @@ struct Header {
   uint32_t magic;
   int32_t version, kind, n_chunks, n_seg, n_work, cp_size, bs;
 };
+static_assert(sizeof(Header) <= kCtrOffset, "the header stays clear of the job counters");
 
 // Work list for one attention call: segments cut into items of q_tile
 // positions, each with the number of key tiles it visits, ordered longest
@@ -80,6 +81,14 @@ void build_work(const std::vector<Seg>& segs, int q_tile, std::vector<Work>& wor
   }
   std::stable_sort(work.begin(), work.end(),
                    [](const Work& a, const Work& b) { return a.n_tiles > b.n_tiles; });
+}
+
+// Mean key tiles per work item, rounded down (0 for an empty list).
+int32_t mean_item_tiles(const std::vector<Work>& work) {
+  if (work.empty()) return 0;
+  int64_t sum = 0;
+  for (const Work& w : work) sum += w.n_tiles;
+  return (int32_t)(sum / (int64_t)work.size());
 }
 
 int check_group(int32_t g, bool allow_zero) {
@@ -278,6 +287,7 @@ extern "C" int cp_meta_build(int32_t cp_size, int32_t cp_rank, int32_t bs,
   m.max_chunk_rows = max_chunk;
   m.n_seg = (int32_t)segs.size();
   m.n_work = (int32_t)work.size();
+  m.mean_item_tiles = mean_item_tiles(work);
   m.max_kv_len = max_kv;
   m.q_tile = q_tile;
   m.kv_align = kKvAlignMax;
@@ -354,6 +364,7 @@ extern "C" int cp_allgather_meta_build(int32_t q_total, int32_t q_real, int32_t 
   m.n_local_rows = q_total;
   m.n_seg = 1;
   m.n_work = (int32_t)work.size();
+  m.mean_item_tiles = mean_item_tiles(work);
   m.max_kv_len = kv_len;
   m.q_tile = q_tile;
   m.kv_align = kKvAlignMax;
@@ -435,6 +446,7 @@ extern "C" int cp_allgather_packed_meta_build(int32_t n_docs, const int32_t* doc
   m.n_local_rows = q_total;
   m.n_seg = (int32_t)segs.size();
   m.n_work = (int32_t)work.size();
+  m.mean_item_tiles = mean_item_tiles(work);
   m.max_kv_len = max_kv;
   m.q_tile = q_tile;
   m.kv_align = align;

@@ -54,7 +54,7 @@ typedef enum cp_status {
   CP_ERR_HIP = -5               /* the HIP runtime reported an error at launch */
 } cp_status_t;
 
-enum { CP_META_VERSION = 2 };
+enum { CP_META_VERSION = 3 };
 enum { CP_META_ZIGZAG = 1, CP_META_ALLGATHER = 2 };
 enum { CP_RERANGE_GATHERED_TO_ORIG = 0, CP_RERANGE_ORIG_TO_GATHERED = 1 };
 
@@ -65,7 +65,11 @@ enum { CP_RERANGE_GATHERED_TO_ORIG = 0, CP_RERANGE_ORIG_TO_GATHERED = 1 };
  * at the listed byte offsets (each offset is a multiple of 256).  The caller
  * reads the lists from the host copy and copies the whole blob (blob_bytes)
  * to a device buffer with hipMemcpyAsync on its stream; the copy and
- * attention calls take that device copy (d_blob) plus this struct.
+ * attention calls take that device copy (d_blob) plus this struct.  The copy
+ * calls only read d_blob.  cp_prefill_attn also updates a 36-byte job-counter
+ * area in its 256-byte header while it runs and leaves it as the builder
+ * wrote it (zero), so two attention launches that share one d_blob must not
+ * run at the same time: order them on one stream, or give each its own copy.
  *
  * Lists of [P5] ZigzagContextParallelMetadata (int32):
  *   split_list[bs*2cp]         block sizes, sequence-major
@@ -100,7 +104,7 @@ typedef struct cp_meta {
   int32_t q_tile;             /* query positions per work item */
   int32_t kv_align;           /* largest power of two (<= 2^30) dividing every segment's first key
                                  position in its page-table row (2^30 when all start at 0) */
-  int32_t reserved;
+  int32_t mean_item_tiles;    /* mean 64-key tiles per work item, rounded down (0: no items) */
   int64_t blob_bytes;         /* bytes of the blob that are in use */
   int64_t off_split_list, off_zigzag_index, off_cp_reverse_index, off_reverse_split_len;
   int64_t off_per_rank_actual_token, off_kv_len_prev, off_kv_len_next;
@@ -265,18 +269,29 @@ int cp_kv_scatter(const void* d_blob, const cp_meta_t* meta,
  *     (whole pages per key tile when it is >= page_size); a meta whose
  *     kv_align overstates the segments' alignment gives unspecified results,
  *     again with no out-of-bounds read.  The meta builders set it exactly.
+ *   Scheduling: one workgroup per job (work item, KV head).  When there are
+ *     more jobs than compute units and items average at least 48 key tiles
+ *     (meta->mean_item_tiles), the first round of jobs (one per compute unit)
+ *     is fixed and the rest are handed out at run time from 8 queues, one per
+ *     XCD, from which an XCD whose own queue is empty takes the next job of
+ *     another's; the grid then holds up to 1/8 more workgroups, which find no
+ *     job and end at once.  The job counters live in d_blob's header (see the
+ *     blob description above): launches that share a blob must not overlap.
+ *     A job's result does not depend on where it runs: outputs are
+ *     bit-identical from launch to launch.
  * Errors: NULL meta or d_blob, unknown meta kind or version, H_q % H_kv != 0
  * ([P4]), H_q/H_kv different from meta->attn_group (the work list's), scale
  * not finite or <= 0, num_pages < 1, NULL or misaligned (16-byte) pointers
  * -> CP_ERR_INVALID_ARG; D not in {64, 128}, H_kv*D*2*64 >= 2^31 (one 64-key
  * tile of all KV heads), page_size not a power of two up to 2^20 ->
- * CP_ERR_UNSUPPORTED; a grid (n_work * H_kv workgroups of 512 threads) of
- * more than 2^23-1 workgroups (HIP's 2^32-1 work-item limit) ->
- * CP_ERR_OVERFLOW; launch failure -> CP_ERR_HIP.
+ * CP_ERR_UNSUPPORTED; a grid (n_work * H_kv workgroups of 512 threads, plus
+ * the spare ones of run-time scheduling) of more than 2^23-1 workgroups
+ * (HIP's 2^32-1 work-item limit) -> CP_ERR_OVERFLOW; a failing query of the
+ * device's compute-unit count or a launch failure -> CP_ERR_HIP.
  */
 int cp_prefill_attn(const void* q, const void* k_pool, const void* v_pool, void* out,
                     int32_t H_q, int32_t H_kv, int32_t D, float scale,
-                    const void* d_blob, const cp_meta_t* meta,
+                    void* d_blob, const cp_meta_t* meta,
                     int32_t num_pages, int32_t page_size, const int32_t* kv_page_indptr,
                     const int32_t* kv_page_indices, hipStream_t stream);
 

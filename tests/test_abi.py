@@ -126,6 +126,8 @@ def test_segments_and_work_list(group):
             assert np.all(seen[s] == 1)       # every row in exactly one item
         nt = work[:, 3]
         assert np.all(nt[:-1] >= nt[1:])      # longest first
+        assert m.mean_item_tiles == int(nt.sum()) // len(nt)
+        assert not np.any(m.blob[128:128 + 36])   # attention job counters start at zero
         # the visited tiles cover every useful (query, key) pair
         assert sum(useful_pairs(s[1], s[3], True) for s in segs) <= \
             sum(int(w[3]) * 64 * int(w[2]) for w in work)
@@ -139,6 +141,7 @@ def test_allgather_meta():
     assert tuple(seg[:7]) == (0, 8192, 8192, 30000, 0, 0, 0)
     work = _unpack(m.blob, m.off_work, m.n_work, 4)
     assert m.n_work == 8192 // (ROWS_PER_ITEM // 4) and np.all(work[:, 3] == -(-30000 // 64))
+    assert m.mean_item_tiles == -(-30000 // 64) and not np.any(m.blob[128:128 + 36])
     m = cpa.allgather_meta_build(100, 70, 33, 32)    # pad query rows 70..99
     work = _unpack(m.blob, m.off_work, m.n_work, 4)
     assert work[:, 2].sum() == 100
