@@ -22,13 +22,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 // for its ticket (one device-scope atomic before a workgroup's first load).
 constexpr int kDynamicMinTiles = 48;
 
-// Compute units of the current device, queried once per device.
-int compute_units(int* n_cu) {
+// Compute units of the device that runs `stream` (the current device for
+// the null stream), queried once per device.
+int compute_units(hipStream_t stream, int* n_cu) {
   static std::mutex mu;
   static std::vector<int> cache;
   int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return set_error(CP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(CP_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
   std::lock_guard<std::mutex> lock(mu);
   if (dev >= (int)cache.size()) cache.resize(dev + 1, 0);
   if (cache[dev] == 0) {
@@ -87,7 +88,7 @@ extern "C" int cp_prefill_attn(const void* q, const void* k_pool, const void* v_
     return set_error(CP_ERR_OVERFLOW, "attention grid too large (%lld workgroups of %d threads)",
                      (long long)n_jobs, kThreads);
   int n_cu = 0;
-  if (int rc = compute_units(&n_cu)) return rc;
+  if (int rc = compute_units(stream, &n_cu)) return rc;
   const bool dynamic = n_jobs > n_cu && meta->mean_item_tiles >= kDynamicMinTiles;
   const int64_t n_static = dynamic ? n_cu : n_jobs;
   const int64_t n_spare = dynamic ? std::max<int64_t>(8, (n_jobs - n_static) / 8) : 0;
