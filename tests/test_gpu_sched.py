@@ -53,11 +53,12 @@ def _jobs_case(n_jobs, h_kv, h_q=32, d=128, kv_len=3072, ps=64, seed=21):
     return qg, kg, vg, meta, kp, vp, indptr, indices, q_tile
 
 
-@pytest.mark.parametrize("extra,h_kv", [(1, 1), (3, 1), (37, 1), (None, 8)])
-def test_runtime_scheduling_every_job_once(extra, h_kv):
+@pytest.mark.parametrize("extra,h_kv,d,ps", [(1, 1, 128, 64), (3, 1, 128, 64), (37, 1, 128, 64), (None, 8, 128, 64),
+                                             (37, 1, 64, 16), (None, 8, 64, 32)])
+def test_runtime_scheduling_every_job_once(extra, h_kv, d, ps):
     n_cu = _n_cu()
     n_jobs = n_cu + extra if extra is not None else -(-(3 * n_cu + 40) // 8) * 8
-    qg, kg, vg, meta, kp, vp, indptr, indices, q_tile = _jobs_case(n_jobs, h_kv)
+    qg, kg, vg, meta, kp, vp, indptr, indices, q_tile = _jobs_case(n_jobs, h_kv, d=d, ps=ps)
     assert n_jobs > n_cu and meta.mean_item_tiles >= 48     # the run-time path is the one taken
     assert _counters(meta) == [0] * CTR_WORDS
     q = qg.cuda()
@@ -65,8 +66,8 @@ def test_runtime_scheduling_every_job_once(extra, h_kv):
     first = None
     for launch in range(3):
         out = torch.full(qg.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
-        print(f"sched n_jobs={n_jobs} h_kv={h_kv} launch {launch}", flush=True)
-        cpa.prefill_attn(q, kp, vp, out, meta, scale, 64, indptr, indices)
+        print(f"sched n_jobs={n_jobs} h_kv={h_kv} d={d} ps={ps} launch {launch}", flush=True)
+        cpa.prefill_attn(q, kp, vp, out, meta, scale, ps, indptr, indices)
         torch.cuda.synchronize()
         assert _counters(meta) == [0] * CTR_WORDS, f"counters left set after launch {launch}"
         assert torch.isfinite(out).all(), "a job was not run (rows still hold the NaN fill)"
