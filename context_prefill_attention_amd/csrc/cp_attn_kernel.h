@@ -709,15 +709,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnArgs a) {
   const float l_tot = wave_half_sum(l_run);   // the two lane halves summed different keys
   const float inv = live ? 1.f / l_tot : 0.f;
   unsigned char* orow = a.out + qrow * D * 2;
+  // Stored as held, each store would write 8 bytes to each of 32 rows, and
+  // the CU issues such stores slowly (the last wave of a workgroup ended
+  // some 3 us after the first).  The lane halves of a row (same validity,
+  // both active) swap 8-byte pieces so that each lane stores 16 bytes: half
+  // 0 gets d 16*jp + 0..7 of block db, half 1 d 16*jp + 8..15, and a wave
+  // issues 8 stores instead of 16.
 #pragma unroll
   for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int d = db * 32 + jj * 8 + half * 4;
-      u32x2 v;
-      v[0] = pack_bf16x2(o[db][jj * 4 + 0] * inv, o[db][jj * 4 + 1] * inv);
-      v[1] = pack_bf16x2(o[db][jj * 4 + 2] * inv, o[db][jj * 4 + 3] * inv);
-      *reinterpret_cast<u32x2*>(orow + d * 2) = v;
+    for (int jp = 0; jp < 2; ++jp) {
+      uint32_t x[2], y[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        x[e] = pack_bf16x2(o[db][jp * 8 + 2 * e] * inv, o[db][jp * 8 + 2 * e + 1] * inv);
+        y[e] = pack_bf16x2(o[db][jp * 8 + 4 + 2 * e] * inv, o[db][jp * 8 + 4 + 2 * e + 1] * inv);
+        auto r = __builtin_amdgcn_permlane32_swap(x[e], y[e], false, false);
+        x[e] = r[0];
+        y[e] = r[1];
+      }
+      const int d = db * 32 + jp * 16 + half * 8;
+      *reinterpret_cast<u32x4*>(orow + d * 2) = u32x4{x[0], x[1], y[0], y[1]};
     }
   clear_counters();
 }
