@@ -201,7 +201,8 @@ def cpu_baseline(w, meta_lists, q_loc, k_seq, v_seq, n_rows: int):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "blas": oracle_blas(),
             "sample": f"{per * len(segs)} query rows ({per} evenly spaced per zigzag half) x {w.h_q} heads "
-                      f"of the same rank share, all visible keys, numpy float64; {dt:.1f} s"}
+                      f"of the same rank share, all visible keys, numpy float64 in one process whose BLAS "
+                      f"runs on `cores` threads; {dt:.1f} s"}
 
 
 def cpu_baseline_copies(w, rank, lens, k_g, indptr, indices, n_pages):
@@ -256,7 +257,8 @@ def cpu_baseline_allgather(w, h_q, q_loc, k_g, v_g, doc_cu, q_start, n_rows: int
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "blas": oracle_blas(),
             "sample": f"{len(rows)} evenly spaced local query rows x {h_q} heads of the same share, "
-                      f"all visible keys, numpy float64; {dt:.1f} s"}
+                      f"all visible keys, numpy float64 in one process whose BLAS runs on `cores` threads; "
+                      f"{dt:.1f} s"}
 
 
 def run_timed(torch, step, names, warmup: int, steps: int):
