@@ -173,10 +173,11 @@ def _prefix_extend_case(cp, lens, prefix, h_q, h_kv, d, ps, seed, sample=None):
         mo = zigzag_meta.build(cp, r, sum(lens), seq_lens=full, extend_lens=lens)
         q_loc = torch.from_numpy(layout.shard(q_ext.view(torch.int16).numpy(), mo)).view(torch.bfloat16)
         meta = cpa.meta_build(cp, r, lens, seq_lens=full, attn_group=h_q // h_kv, device="cuda")
-        out = torch.empty(q_loc.shape, dtype=torch.bfloat16, device="cuda")
+        out = torch.full(q_loc.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
         cpa.prefill_attn(q_loc.cuda(), kp, vp, out, meta, 1 / math.sqrt(d), ps, torch.from_numpy(indptr).cuda(),
                          torch.from_numpy(indices).cuda())
         torch.cuda.synchronize()
+        assert torch.isfinite(out).all(), f"prefix rank {r}: rows left unwritten"   # every job ran
         if sample is None:
             ref = oatt.zigzag_rank(q_loc, k_seqs, v_seqs, mo, 1 / math.sqrt(d))
             gc.assert_close(out, ref, f"prefix rank {r}")
