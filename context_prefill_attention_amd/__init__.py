@@ -86,8 +86,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                   _vp, _vp, _vp]
     lib.cp_prefill_attn.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, ctypes.c_float, _vp,
                                     P(CMeta), _i32, _i32, _vp, _vp, _vp]
+    lib.cp_prefill_attn_noalloc.argtypes = lib.cp_prefill_attn.argtypes
     for fn in ("cp_meta_build", "cp_allgather_meta_build", "cp_allgather_packed_meta_build",
-               "cp_zigzag_rerange", "cp_zigzag_rerange_kv", "cp_kv_scatter", "cp_prefill_attn"):
+               "cp_zigzag_rerange", "cp_zigzag_rerange_kv", "cp_kv_scatter", "cp_prefill_attn",
+               "cp_prefill_attn_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.cp_last_error.restype = ctypes.c_char_p
     lib.cp_last_error.argtypes = []
@@ -383,14 +385,16 @@ def kv_scatter(meta: Meta, k_gathered, v_gathered, k_pool, v_pool, page_size: in
 
 
 def prefill_attn(q, k_pool, v_pool, out, meta: Meta, scale: float, page_size: int,
-                 kv_page_indptr, kv_page_indices) -> None:
+                 kv_page_indptr, kv_page_indices, noalloc: bool = False) -> None:
     """``cp_prefill_attn`` on the current stream.
 
     q, out: [n_local_rows, H_q, D] bf16; k_pool, v_pool: [num_pages,
     page_size, H_kv, D] bf16 (a contiguous [S, H_kv, D] tensor can be viewed
     as pages with the identity page table).  The launch uses job counters in
     the header of ``meta.d_blob`` and leaves them zero, so two attention
-    launches with the same device blob must not run concurrently."""
+    launches with the same device blob must not run concurrently.  With
+    ``noalloc`` it calls ``cp_prefill_attn_noalloc``: the counters live in the
+    library's per-device array instead and the blob is only read."""
     import torch
     lib = load_library()
     n, h_q, d = q.shape
@@ -402,7 +406,8 @@ def prefill_attn(q, k_pool, v_pool, out, meta: Meta, scale: float, page_size: in
     if kv_page_indptr.numel() != meta.bs + 1:
         raise CpError(CP_ERR_INVALID_ARG, "kv_page_indptr must have bs+1 entries")
     bf = torch.bfloat16
-    _check(lib.cp_prefill_attn(
+    fn = lib.cp_prefill_attn_noalloc if noalloc else lib.cp_prefill_attn
+    _check(fn(
         _dev_tensor(q, "q", bf), _dev_tensor(k_pool, "k_pool", bf), _dev_tensor(v_pool, "v_pool", bf),
         _dev_tensor(out, "out", bf), h_q, h_kv, d, float(scale), _need_device(meta),
         ctypes.byref(meta.c), num_pages, page_size,

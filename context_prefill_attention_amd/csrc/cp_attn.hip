@@ -43,16 +43,49 @@ int compute_units(hipStream_t stream, int* n_cu) {
   return CP_OK;
 }
 
-}  // namespace
-}  // namespace cpattn
+// Job counters of cp_prefill_attn_noalloc: one array per device (each GPU
+// holds its own copy for the life of the process), zero at load and left zero
+// by every launch.  In host code `scratch` names a host-side stand-in; the
+// kernels get the device address that hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned int scratch[kCtrWords];
 
-using namespace cpattn;
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+int scratch_address(hipStream_t stream, unsigned int** out) {
+  static std::mutex mu;
+  static std::vector<unsigned int*> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(CP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (stream) {
+    int sdev = 0;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return set_error(CP_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
+    if (sdev != dev)
+      return set_error(CP_ERR_INVALID_ARG, "the stream belongs to device %d, the current device is %d",
+                       sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= (int)cache.size()) cache.resize(dev + 1, nullptr);
+  if (!cache[dev]) {
+    unsigned int* p = nullptr;
+    e = hipGetSymbolAddress(reinterpret_cast<void**>(&p), HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(CP_ERR_HIP, "address of the job counters on device %d: %s", dev, hipGetErrorString(e));
+    cache[dev] = p;
+  }
+  *out = cache[dev];
+  return CP_OK;
+}
 
-extern "C" int cp_prefill_attn(const void* q, const void* k_pool, const void* v_pool, void* out,
-                               int32_t H_q, int32_t H_kv, int32_t D, float scale,
-                               void* d_blob, const cp_meta_t* meta,
-                               int32_t num_pages, int32_t page_size, const int32_t* kv_page_indptr,
-                               const int32_t* kv_page_indices, hipStream_t stream) {
+// Where a launch keeps its job counters.
+enum class CtrHome { kBlob, kStatic };
+
+// Validation, scheduling and launch shared by both entry points.
+int prefill_attn(const void* q, const void* k_pool, const void* v_pool, void* out, int32_t H_q,
+                 int32_t H_kv, int32_t D, float scale, const void* d_blob, const cp_meta_t* meta,
+                 int32_t num_pages, int32_t page_size, const int32_t* kv_page_indptr,
+                 const int32_t* kv_page_indices, hipStream_t stream, CtrHome home) {
   clear_error();
   if (!meta || !d_blob) return set_error(CP_ERR_INVALID_ARG, "meta or d_blob is NULL");
   if (meta->version != CP_META_VERSION ||
@@ -96,13 +129,20 @@ extern "C" int cp_prefill_attn(const void* q, const void* k_pool, const void* v_
   if (grid > 4294967295LL / kThreads)
     return set_error(CP_ERR_OVERFLOW, "attention grid too large (%lld workgroups of %d threads)",
                      (long long)grid, kThreads);
+  unsigned int* ctr = nullptr;
+  if (home == CtrHome::kStatic) {
+    if (int rc = scratch_address(stream, &ctr)) return rc;
+  } else {
+    // the caller's blob, written by this launch (the public entry point takes it non-const)
+    ctr = reinterpret_cast<unsigned int*>(const_cast<char*>(static_cast<const char*>(d_blob)) + kCtrOffset);
+  }
   AttnArgs args;
   args.q = static_cast<const unsigned char*>(q);
   args.k_pool = static_cast<const unsigned char*>(k_pool);
   args.v_pool = static_cast<const unsigned char*>(v_pool);
   args.out = static_cast<unsigned char*>(out);
-  char* base = static_cast<char*>(d_blob);
-  args.ctr = reinterpret_cast<unsigned int*>(base + kCtrOffset);
+  const char* base = static_cast<const char*>(d_blob);
+  args.ctr = ctr;
   args.n_jobs = (int32_t)n_jobs;
   args.n_static = (int32_t)n_static;
   args.segs = reinterpret_cast<const Seg*>(base + meta->off_segs);
@@ -142,4 +182,28 @@ extern "C" int cp_prefill_attn(const void* q, const void* k_pool, const void* v_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(CP_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   return CP_OK;
+}
+
+}  // namespace
+}  // namespace cpattn
+
+using namespace cpattn;
+
+extern "C" int cp_prefill_attn(const void* q, const void* k_pool, const void* v_pool, void* out,
+                               int32_t H_q, int32_t H_kv, int32_t D, float scale,
+                               void* d_blob, const cp_meta_t* meta,
+                               int32_t num_pages, int32_t page_size, const int32_t* kv_page_indptr,
+                               const int32_t* kv_page_indices, hipStream_t stream) {
+  return prefill_attn(q, k_pool, v_pool, out, H_q, H_kv, D, scale, d_blob, meta, num_pages, page_size,
+                      kv_page_indptr, kv_page_indices, stream, CtrHome::kBlob);
+}
+
+extern "C" int cp_prefill_attn_noalloc(const void* q, const void* k_pool, const void* v_pool, void* out,
+                                       int32_t H_q, int32_t H_kv, int32_t D, float scale,
+                                       const void* d_blob, const cp_meta_t* meta,
+                                       int32_t num_pages, int32_t page_size,
+                                       const int32_t* kv_page_indptr, const int32_t* kv_page_indices,
+                                       hipStream_t stream) {
+  return prefill_attn(q, k_pool, v_pool, out, H_q, H_kv, D, scale, d_blob, meta, num_pages, page_size,
+                      kv_page_indptr, kv_page_indices, stream, CtrHome::kStatic);
 }

@@ -295,6 +295,29 @@ int cp_prefill_attn(const void* q, const void* k_pool, const void* v_pool, void*
                     int32_t num_pages, int32_t page_size, const int32_t* kv_page_indptr,
                     const int32_t* kv_page_indices, hipStream_t stream);
 
+/*
+ * cp_prefill_attn_noalloc -- for callers that cannot allocate device memory
+ * for a launch's working state or must not have their metadata written (code
+ * under HIP graph capture that treats the blob as read-only, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, computation,
+ * results (bit for bit) and errors as cp_prefill_attn, but d_blob is only
+ * read: the run-time job counters live in a file-scope device array of the
+ * library (9 words, 36 bytes, fixed: no input size needs more; each GPU holds
+ * its own copy until the process ends).  Its device address is looked up
+ * once per device (hipGetSymbolAddress, with that device current); nothing
+ * is allocated, here or later.  Every launch leaves the counters zero, the
+ * state the next launch needs.  All calls on one GPU share the array, so
+ * calls that overlap in time on one GPU race and give wrong results: order
+ * them on one stream.
+ * Extra errors: the stream belonging to a device other than the current one
+ * -> CP_ERR_INVALID_ARG; a failing symbol lookup -> CP_ERR_HIP.
+ */
+int cp_prefill_attn_noalloc(const void* q, const void* k_pool, const void* v_pool, void* out,
+                            int32_t H_q, int32_t H_kv, int32_t D, float scale,
+                            const void* d_blob, const cp_meta_t* meta,
+                            int32_t num_pages, int32_t page_size, const int32_t* kv_page_indptr,
+                            const int32_t* kv_page_indices, hipStream_t stream);
+
 /* Thread-local description of the last error of this thread ("" if none). */
 const char* cp_last_error(void);
 

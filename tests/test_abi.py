@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol(lib):
     names = set(re.findall(r"^\s*(?:int|const char\*)\s+(cp_\w+)\s*\(", text, flags=re.M))
     assert {"cp_meta_build", "cp_allgather_meta_build", "cp_allgather_packed_meta_build",
             "cp_zigzag_rerange", "cp_zigzag_rerange_kv", "cp_kv_scatter",
-            "cp_prefill_attn", "cp_last_error", "cp_version"} <= names
+            "cp_prefill_attn", "cp_prefill_attn_noalloc", "cp_last_error", "cp_version"} <= names
     for n in names:
         assert hasattr(lib, n), n   # ctypes dlsym succeeds
 
@@ -278,6 +278,22 @@ def fake_ok(lib):
 def _attn(lib, m, h_q=32, h_kv=4, d=128, scale=0.088, ps=16, q=FAKE, npages=10):
     return lib.cp_prefill_attn(q, FAKE, FAKE, FAKE, h_q, h_kv, d, scale, FAKE, ctypes.byref(m.c),
                                npages, ps, FAKE, FAKE, None)
+
+
+def test_noalloc_attention_validation_fails_closed(fake_ok):
+    """The no-allocation variant validates exactly as cp_prefill_attn, before
+    it looks anything up on the device."""
+    lib = fake_ok
+    m = cpa.meta_build(2, 0, [64], attn_group=8)
+    call = lambda h_q=32, h_kv=4, d=128, blob=FAKE: lib.cp_prefill_attn_noalloc(
+        FAKE, FAKE, FAKE, FAKE, h_q, h_kv, d, 0.088, blob, ctypes.byref(m.c), 10, 16, FAKE, FAKE, None)
+    assert call(h_kv=5) == cpa.CP_ERR_INVALID_ARG and b"multiple" in lib.cp_last_error()
+    assert call(d=96) == cpa.CP_ERR_UNSUPPORTED
+    assert call(blob=None) == cpa.CP_ERR_INVALID_ARG
+    big = cpa.meta_build(2, 0, [64], attn_group=8)
+    big.c.n_work = (1 << 23) // 8
+    assert lib.cp_prefill_attn_noalloc(FAKE, FAKE, FAKE, FAKE, 64, 8, 128, ctypes.c_float(0.088), FAKE,
+                                       ctypes.byref(big.c), 4, 16, FAKE, FAKE, None) == cpa.CP_ERR_OVERFLOW
 
 
 def test_attention_validation_fails_closed(fake_ok):
