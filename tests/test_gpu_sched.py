@@ -137,3 +137,44 @@ def test_runtime_scheduling_in_a_graph():
         step()   # eager launch between replays
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"eager after replay {rep}"
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_runtime_scheduling_random_shapes(seed):
+    """Seeded AllGather-KV shapes with 1-4 rounds of jobs beyond the CU count,
+    every head grouping, D 64/128, pages of 16/64 and a ragged last item: two
+    launches of each entry point give the same bits, every row is written,
+    the blob counters are zero after each, and sampled rows match the oracle."""
+    rng = np.random.default_rng(9000 + seed)
+    n_cu = _n_cu()
+    h_kv = int(rng.choice([1, 2, 4, 8]))
+    group = int(rng.choice([1, 2, 4, 8]))
+    h_q, d, ps = h_kv * group, int(rng.choice([64, 128])), int(rng.choice([16, 64]))
+    q_tile = ROWS_PER_ITEM // group
+    n_items = int(rng.integers(n_cu // h_kv + 1, 4 * n_cu // h_kv + 2))
+    q_total = n_items * q_tile - int(rng.integers(0, q_tile))
+    kv_len = int(rng.integers(3072, 8193))
+    npages = -(-kv_len // ps)
+    qg, kg, vg = synth.normal_bf16(9100 + seed, (q_total, h_q, d), (npages * ps, h_kv, d), (npages * ps, h_kv, d))
+    meta = cpa.allgather_meta_build(q_total, q_total, kv_len, group, device="cuda")
+    assert meta.n_work * h_kv > n_cu and meta.mean_item_tiles >= 48
+    print(f"sched random {seed}: H {h_q}/{h_kv} d {d} ps {ps} rows {q_total} keys {kv_len} "
+          f"jobs {meta.n_work * h_kv}", flush=True)
+    kp, vp = kg.view(npages, ps, h_kv, d).cuda(), vg.view(npages, ps, h_kv, d).cuda()
+    ip = torch.tensor([0, npages], dtype=torch.int32, device="cuda")
+    ix = torch.arange(npages, dtype=torch.int32, device="cuda")
+    q, scale = qg.cuda(), 1 / math.sqrt(d)
+    outs = []
+    for _launch in range(2):
+        for noalloc in (False, True):
+            out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+            cpa.prefill_attn(q, kp, vp, out, meta, scale, ps, ip, ix, noalloc=noalloc)
+            torch.cuda.synchronize()
+            assert torch.isfinite(out).all(), "a job was not run"
+            assert _counters(meta) == [0] * CTR_WORDS
+            outs.append(out)
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    rows = sorted({0, q_total - 1} | set(rng.integers(0, q_total, 4).tolist()))
+    gc.assert_close(outs[0][rows], oatt.allgather_kv(qg, kg, vg, q_total, kv_len, scale, rows=rows),
+                    f"sched random {seed}")
